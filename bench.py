@@ -1,0 +1,197 @@
+"""W12 GEMM benchmark on one MI355X.
+
+Workload (one step): the MLP GEMMs at hidden size 5120 - gate and up
+(17408 x 5120) and down (5120 x 17408) - as exact W12 GEMMs with fp32
+accumulation and BF16 output, at M = 1 and M = 32 activation rows: six GEMM
+calls per step. Weights are synthetic per-output-channel Gaussians (per-row
+lognormal scales, 1e-4 outliers x 2^12, 1e-4 zeros), encoded on the GPU
+before timing; activations are BF16 N(0, 1). Every input is resident in HBM
+before the timed region. Each step rotates through R encoded copies of each
+matrix (R * 401 MB well above the 256 MB last-level cache), so weights
+stream from HBM, as in the pages' cold-L2 measurements.
+
+Prints one JSON line: value = packed W12 bytes (1.5 B per weight) streamed
+per second over the whole step, plus per-call figures, the roofline entry of
+the dominant kernel and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W12 GEMM achieved HBM GB/s (% of peak) and µs/call at M=1 and M=32"
+PEAK_GBS = 8000.0
+MS = (1, 32)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--copies", type=int, default=4, help="encoded copies of each matrix to rotate through")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of each matrix in the CPU oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--ms", type=str, default=None, help="comma-separated M values (default 1,32)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the W12 GEMM shards along output channels with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from lossless_compressed_weight_amd import w12
+
+    ms = tuple(int(v) for v in args.ms.split(",")) if args.ms else MS
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    wl = synth.WORKLOADS[1]
+    t0 = time.time()
+    mats_host = [(spec.name, synth.workload_matrix(1, i)) for i, spec in enumerate(wl.matrices)]
+    print(f"# generated weights in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    encoded = []   # per matrix: list of R W12Matrix copies
+    for name, w in mats_host:
+        wd = torch.from_numpy(w.view(np.int16)).to(dev)
+        mat = w12.encode(wd)
+        del wd
+        copies = [mat] + [w12.W12Matrix(mat.n, mat.k, mat.records.clone(), mat.e_top.clone(),
+                                        mat.row_ptr.clone(), mat.esc.clone(), mat.n_esc)
+                          for _ in range(args.copies - 1)]
+        encoded.append(copies)
+    torch.cuda.synchronize()
+    print(f"# encoded {len(encoded)} matrices x {args.copies} copies", file=sys.stderr, flush=True)
+
+    xs_host = {m: synth.make_activations(m, 17408, seed=synth.activation_seed(1, 0, m)) for m in ms}
+    calls = []     # (m, matrix index, x view, y, ws)
+    for m in ms:
+        for i, (name, w) in enumerate(mats_host):
+            n, k = w.shape
+            x = torch.from_numpy(xs_host[m][:, :k].copy().view(np.int16)).to(dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            nb = w12.workspace_bytes(w12.OP_GEMM, n, k, m)
+            ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+            calls.append((m, i, x, y, ws))
+    stream = torch.cuda.current_stream()
+
+    def run_step(step, events=None):
+        c = step % args.copies
+        for j, (m, i, x, y, ws) in enumerate(calls):
+            if events is not None:
+                events[j][0].record(stream)
+            w12.w12_gemm(encoded[i][c], x, y, ws, stream)
+            if events is not None:
+                events[j][1].record(stream)
+
+    for s in range(args.warmup):
+        run_step(s)
+    torch.cuda.synchronize()
+
+    # timed region: K steps; per-call HIP events on the launch stream
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in calls]
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        run_step(args.warmup + s, ev[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    per_call = []
+    packed_step = 0
+    for j, (m, i, x, y, ws) in enumerate(calls):
+        name, w = mats_host[i]
+        n, k = w.shape
+        t = [ev[s][j][0].elapsed_time(ev[s][j][1]) * 1e3 for s in range(args.steps)]  # us
+        mat = encoded[i][0]
+        packed = n * k * 3 // 2
+        algo = packed + n + 4 * (n + 1) + 8 * mat.n_esc + 2 * m * k + 2 * m * n
+        med = float(np.median(t))
+        per_call.append({"m": m, "matrix": name, "n": n, "k": k, "us_median": round(med, 3),
+                         "us_p10": round(float(np.percentile(t, 10)), 3),
+                         "us_p90": round(float(np.percentile(t, 90)), 3),
+                         "us_mean": round(float(np.mean(t)), 3),
+                         "packed_gbs": round(packed / med / 1e3, 1),
+                         "pct_peak_packed": round(100 * packed / med / 1e3 / PEAK_GBS, 2),
+                         "algo_bytes": algo, "n_esc": mat.n_esc,
+                         "path": "gemv" if m < 16 else "mfma"})
+        packed_step += packed
+    value = packed_step / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the GEMM path taking the most time per step
+    by_path = {}
+    for pc in per_call:
+        by_path.setdefault(pc["path"], []).append(pc)
+    dom_path = max(by_path, key=lambda p: sum(pc["us_mean"] for pc in by_path[p]))
+    dom = by_path[dom_path]
+    algo_bytes = sum(pc["algo_bytes"] for pc in dom)
+    dur_us = sum(pc["us_mean"] for pc in dom)
+    achieved = algo_bytes / dur_us / 1e3
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                "kernel": f"w12 {dom_path} GEMM (M={dom[0]['m']}, gate/up/down), mean of per-call HIP events"}
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle as o
+        encs = []
+        for name, w in mats_host:
+            r = min(args.cpu_rows, w.shape[0])
+            encs.append(o.encode(w[:r]))
+        sub = [(name, w[: args.cpu_rows]) for name, w in mats_host]
+        cpu = cpu_baseline(sub, encs, {m: xs_host[m] for m in ms}, args.cpu_rows)
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "MLP W12 GEMMs at hidden 5120: gate/up 17408x5120, down 5120x17408; "
+                                  f"M in {list(ms)}; fp32 accumulate, BF16 out; {args.copies} rotating copies",
+                      "global_batch": list(ms), "seq_len": 1, "parallelism": "none"},
+           "pct_peak": round(100 * value / PEAK_GBS, 2),
+           "per_call": per_call, "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(sub, encs, xs, rows):
+    """The oracle (NumPy decode of the records + float64 matmul) on the first
+    `rows` rows of each matrix, for each M: packed GB/s of that sample."""
+    import oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t_total = 0.0
+    bytes_total = 0
+    for (name, w), enc in zip(sub, encs):
+        for m, x in xs.items():
+            t0 = time.perf_counter()
+            wd = o.decode(enc)
+            o.gemm_ref(x[:, : w.shape[1]], wd)
+            t_total += time.perf_counter() - t0
+            bytes_total += w.shape[0] * w.shape[1] * 3 // 2
+    return {"value": round(bytes_total / t_total / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {rows} rows of gate, up and down at M in {list(xs)}: oracle decode of the "
+                      f"records + float64 matmul ({t_total:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

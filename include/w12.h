@@ -1,0 +1,195 @@
+/*
+ * w12.h - C ABI of libw12, the MI355X (gfx950) implementation of the W12
+ * lossless 12-bit weight format and its weight-read-bound skinny GEMM.
+ *
+ * Source of the method: "SpecPilot: Autonomous Algorithm Discovery and Systems
+ * Optimization for Speculative Decoding" (arXiv 2611.02501), section 4.1
+ * "W12: A Lossless 12-bit Weight Format" and Figure 5 (format, escapes, the
+ * decode-in-register GEMM, deterministic stream-K), section 4.3 "Two-Level
+ * Verification" (the Q pass over the nested 8-bit view), Appendix E "W12
+ * Details" (the W12 LM head).
+ *
+ * ---------------------------------------------------------------- FORMAT v1
+ * A weight matrix W is BF16 [N, K], row-major, one output channel per row
+ * (y = x W^T). N % 16 == 0 and K % 512 == 0.
+ *
+ * Per row n the encoder picks E_n, the top of the 16-binade exponent window
+ * [E_n - 15, E_n] holding the most normal weights (exponent field 1..254).
+ * Ties go to the largest such top not above the row's largest normal exponent;
+ * a row with no normal weight gets 16. E_n is in [16, 254]; it is stored as
+ * e_top[n] (uint8).
+ *
+ * An in-window weight with sign s, exponent field e and mantissa m keeps
+ *     off = e - (E_n - 15)   (4 bits, plane E)
+ *     mh  = m >> 4           (3 bits, plane A together with s)
+ *     ml  = m & 15           (4 bits, plane B)
+ * and its 8-bit view byte is  v = s << 7 | off << 3 | mh.
+ * Every other weight (below or above the window, +-0, subnormal, inf, NaN) is
+ * an ESCAPE: its planes hold a placeholder, the in-window value nearest to it
+ * with its sign - (s,15,7,15) above the window and for inf/NaN, (s,0,0,0)
+ * otherwise - and the escape list keeps its exact bits.
+ *
+ * Records: 12288 bytes for 16 rows x 512 columns, stored in (row block
+ * n / 16, column block k / 512) row-major order. Inside a record, row r and
+ * column c = 16 G + t (G in 0..31, t in 0..15):
+ *     view byte  at  (G*16 + r)*16 + t                         bytes [0, 8192)
+ *     B nibble   in  8192 + (G*16 + r)*8 + (t/8)*4 + (t%4)     bytes [8192, 12288)
+ *                    high nibble when t%8 < 4, low nibble otherwise.
+ * The view (planes A and E) is therefore the first two thirds of every record
+ * and the Q pass reads only it.
+ *
+ * Escapes: CSR by row. esc_row_ptr[N+1] (uint32) and 8-byte entries
+ * { uint32 col; uint16 bits (original BF16); uint16 ph (placeholder BF16) },
+ * columns ascending within a row.
+ *
+ * Encoded size: 1.5 N K + N + 4 (N + 1) + 8 n_esc bytes.
+ *
+ * ---------------------------------------------------------------- CONVENTIONS
+ * - Every tensor pointer is a DEVICE pointer owned by the caller. Host pointers
+ *   are the w12_matrix descriptor itself and n_esc_host. The library never
+ *   allocates, frees or retains memory.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *   are asynchronous on it, except w12_encode_plan and w12_validate, which
+ *   synchronize it. Inputs must stay valid until the stream work completes.
+ * - Every argument is checked before any launch; on error nothing is launched
+ *   and a negative status is returned. No C++ exception crosses the ABI.
+ * - Results are deterministic: the same inputs and shape give the same bits
+ *   (the K reduction is split over workgroups in a fixed order that depends
+ *   only on N, K and M).
+ * - Concurrent calls need distinct workspaces. Workspaces need no
+ *   initialisation and hold nothing between calls.
+ * - W12_E_HIP: a HIP call failed; w12_last_error() names it (thread-local).
+ */
+#ifndef W12_H
+#define W12_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W12_ABI_VERSION 1
+#define W12_FORMAT_VERSION 1
+
+#define W12_REC_ROWS 16
+#define W12_REC_COLS 512
+#define W12_REC_BYTES 12288
+#define W12_REC_VIEW_BYTES 8192
+#define W12_MAX_M 64
+
+/* status codes */
+#define W12_OK 0
+#define W12_E_INVALID_ARG (-1)       /* null pointer, bad dtype, bad leading dimension */
+#define W12_E_UNSUPPORTED_SHAPE (-2) /* N % 16, K % 512, N, K <= 0, K > 2^23, N*K >= 2^32 */
+#define W12_E_M_RANGE (-3)           /* M outside 1..64                                */
+#define W12_E_WORKSPACE (-4)         /* workspace missing or smaller than required     */
+#define W12_E_VERSION (-5)           /* descriptor format_version != W12_FORMAT_VERSION */
+#define W12_E_HIP (-6)               /* a HIP runtime call failed                      */
+#define W12_E_NOT_IMPLEMENTED (-7)
+#define W12_E_CORRUPT (-8)           /* w12_validate found a broken descriptor         */
+
+/* output dtypes */
+#define W12_BF16 0 /* y[m, n] = RNE_bf16(fp32 accumulation) */
+#define W12_F32 1  /* y[m, n] = fp32 accumulation           */
+
+/* workspace queries */
+#define W12_OP_ENCODE_PLAN 1
+#define W12_OP_GEMM 2
+#define W12_OP_GEMM_Q8 3
+#define W12_OP_LMHEAD_ARGMAX 4
+
+/* w12_gemm_q8 flags */
+#define W12_Q8_APPLY_ESCAPES 1u
+
+typedef struct {
+  uint32_t col;  /* column k of the escape                    */
+  uint16_t bits; /* its original BF16 bits                    */
+  uint16_t ph;   /* the placeholder BF16 its planes decode to */
+} w12_escape;
+
+typedef struct {
+  int64_t n, k;                /* out features (N % 16 == 0), in features (K % 512 == 0) */
+  const uint8_t* records;      /* (N/16)*(K/512)*12288 bytes, 16-byte aligned            */
+  const uint8_t* e_top;        /* [N], values 16..254                                    */
+  const uint32_t* esc_row_ptr; /* [N+1], esc_row_ptr[0] == 0, nondecreasing              */
+  const w12_escape* esc;       /* [n_esc], may be NULL when n_esc == 0                   */
+  int64_t n_esc;
+  uint32_t format_version;     /* W12_FORMAT_VERSION                                     */
+} w12_matrix;
+
+int w12_abi_version(void);
+const char* w12_status_str(int status);
+/* Text of the last W12_E_HIP failure on the calling thread ("" if none). */
+const char* w12_last_error(void);
+
+/* Bytes of workspace `op` needs for an N x K matrix and M activation rows
+ * (M is ignored for W12_OP_ENCODE_PLAN). 0 means no workspace is needed.
+ * Returns 0 as well for arguments the op would reject. */
+size_t w12_workspace_bytes(int op, int64_t n, int64_t k, int64_t m);
+
+/* Encode, step 1 (section 4.1: per-channel window choice). Reads w (BF16
+ * [N, K], device, 16-byte aligned, row-major), writes e_top[N] and
+ * esc_row_ptr[N+1] (device), and stores the total number of escapes in
+ * *n_esc_host (host). SYNCHRONIZES the stream (the escape count sizes the
+ * escape buffer). ws: w12_workspace_bytes(W12_OP_ENCODE_PLAN, n, k, 0). */
+int w12_encode_plan(const uint16_t* w, int64_t n, int64_t k, uint8_t* e_top, uint32_t* esc_row_ptr,
+                    int64_t* n_esc_host, void* ws, size_t ws_bytes, void* stream);
+
+/* Encode, step 2 (section 4.1 and Figure 5: split into planes, pack records,
+ * list escapes). Inputs w, e_top, esc_row_ptr as produced by w12_encode_plan;
+ * outputs records ((N/16)*(K/512)*12288 bytes, 16-byte aligned) and esc
+ * (esc_row_ptr[N] entries; may be NULL if that is 0). */
+int w12_encode(const uint16_t* w, int64_t n, int64_t k, const uint8_t* e_top, const uint32_t* esc_row_ptr,
+               uint8_t* records, w12_escape* esc, void* stream);
+
+/* Exact decode (section 4.1: the load-time bit-for-bit check): writes the
+ * original BF16 matrix [N, K] (row-major, 16-byte aligned) to w_out. */
+int w12_decode(const w12_matrix* m, uint16_t* w_out, void* stream);
+
+/* Exact W12 GEMM (section 4.1, Figure 5b): y[M, N] = x[M, K] W^T with fp32
+ * accumulation, escapes fixed up exactly before the output rounding.
+ * x: BF16, row stride ldx >= K elements, 16-byte aligned rows.
+ * y: BF16 or fp32 (y_dtype), row stride ldy >= N elements.
+ * 1 <= M <= 64: M < 16 runs the wavefront GEMV kernel, M >= 16 the MFMA kernel.
+ * ws: w12_workspace_bytes(W12_OP_GEMM, n, k, M) bytes (device). */
+int w12_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,
+             int y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Q pass (section 4.3, zero-copy Q pass): the same product over the 8-bit
+ * view only - the first 8 KB of each record - with the four dropped mantissa
+ * bits set to their midpoint (binary 1000). Escapes keep their placeholders
+ * unless flags has W12_Q8_APPLY_ESCAPES. Arguments as w12_gemm;
+ * ws: w12_workspace_bytes(W12_OP_GEMM_Q8, n, k, M). */
+int w12_gemm_q8(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,
+                int y_dtype, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/* W12 LM head fused with a per-row argmax (Appendix E: the LM head converted
+ * to W12): idx[i] = the lowest n attaining max_n (x W^T)[i, n], computed on
+ * the fp32 logits after the escape fix-up. max_logit (nullable) receives
+ * that fp32 maximum. idx and max_logit are device arrays of M entries.
+ * ws: w12_workspace_bytes(W12_OP_LMHEAD_ARGMAX, n, k, M). */
+int w12_lmhead_argmax(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, int32_t* idx,
+                      float* max_logit, void* ws, size_t ws_bytes, void* stream);
+
+/* Checks a descriptor's device arrays: e_top in [16, 254], esc_row_ptr
+ * starting at 0, nondecreasing and ending at n_esc, escape columns < K and
+ * strictly ascending within each row. SYNCHRONIZES the stream.
+ * ws: 4 bytes of device memory. Returns W12_OK or W12_E_CORRUPT. */
+int w12_validate(const w12_matrix* m, void* ws, size_t ws_bytes, void* stream);
+
+/* Test and tuning hooks (process-wide, not thread-safe; call before launching).
+ * W12_TUNE_PATH: 0 = choose by M, 1 = force the GEMV kernel (M <= 15 only is
+ *   the default range; forcing allows up to 16), 2 = force the MFMA kernel.
+ * W12_TUNE_GRID: workgroup count for the GEMM kernels (0 = default).
+ * Changing W12_TUNE_GRID changes the fp32 summation order and the workspace
+ * size; query w12_workspace_bytes after setting it. Returns the old value. */
+#define W12_TUNE_PATH 1
+#define W12_TUNE_GRID 2
+int64_t w12_set_tuning(int key, int64_t value);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W12_H */

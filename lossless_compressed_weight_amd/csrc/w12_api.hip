@@ -1,0 +1,223 @@
+// C ABI of libw12 (declared in include/w12.h): argument checks, workspace
+// sizing and dispatch to the gfx950 kernels. Every check runs before any HIP
+// call, so invalid arguments never launch anything.
+#include <string.h>
+
+#include <string>
+
+#include "w12_internal.h"
+
+using namespace w12;
+
+namespace {
+
+thread_local std::string g_last_error;
+int g_tune_path = 0;
+int64_t g_tune_grid = 0;
+
+int hip_fail(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+  return W12_E_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// N % 16, K % 512, sizes that fit the kernels' 32-bit indices.
+int check_shape(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0 || n % W12_REC_ROWS != 0 || k % W12_REC_COLS != 0) return W12_E_UNSUPPORTED_SHAPE;
+  if (n > (int64_t)1 << 28 || k > (int64_t)1 << 23 || n * k > (int64_t)0xFFFFFFFFll) return W12_E_UNSUPPORTED_SHAPE;
+  return W12_OK;
+}
+
+int check_matrix(const w12_matrix* m) {
+  if (!m) return W12_E_INVALID_ARG;
+  if (m->format_version != W12_FORMAT_VERSION) return W12_E_VERSION;
+  const int s = check_shape(m->n, m->k);
+  if (s != W12_OK) return s;
+  if (!m->records || !m->e_top || !m->esc_row_ptr || m->n_esc < 0) return W12_E_INVALID_ARG;
+  if (m->n_esc > 0 && !m->esc) return W12_E_INVALID_ARG;
+  if (m->n_esc > m->n * m->k) return W12_E_INVALID_ARG;
+  if (!aligned16(m->records)) return W12_E_INVALID_ARG;
+  return W12_OK;
+}
+
+int check_gemm_args(const w12_matrix* m, const void* x, int64_t M, int64_t ldx, const void* y, int64_t ldy,
+                    int y_dtype) {
+  int s = check_matrix(m);
+  if (s != W12_OK) return s;
+  if (M < 1 || M > W12_MAX_M) return W12_E_M_RANGE;
+  if (!x || !y) return W12_E_INVALID_ARG;
+  if (ldx < m->k || ldx % 8 != 0 || !aligned16(x)) return W12_E_INVALID_ARG;
+  if (ldy < m->n) return W12_E_INVALID_ARG;
+  if (y_dtype != W12_BF16 && y_dtype != W12_F32) return W12_E_INVALID_ARG;
+  return W12_OK;
+}
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t gemm_ws_bytes(const GemmPlan& pl) { return round256(pl.part_bytes) + round256(pl.key_bytes); }
+
+GemmPlan make_plan(int64_t n, int64_t k, int64_t M, int op) {
+  return plan_gemm(n, k, M, op, g_tune_path, g_tune_grid);
+}
+
+int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
+             int op, bool fix, void* ws, size_t ws_bytes, int32_t* idx, float* maxv, void* stream) {
+  const GemmPlan pl = make_plan(m->n, m->k, M, op);
+  if (!pl.mfma && M > 16) return W12_E_M_RANGE;
+  const size_t need = gemm_ws_bytes(pl);
+  if (need > 0 && (!ws || ws_bytes < need)) return W12_E_WORKSPACE;
+  GemmParams p{};
+  p.rec = m->records;
+  p.e_top = m->e_top;
+  p.row_ptr = m->esc_row_ptr;
+  p.esc = reinterpret_cast<const uint2*>(m->esc);
+  p.x = x;
+  p.ldx = ldx;
+  p.y = y;
+  p.ldy = ldy;
+  p.part = reinterpret_cast<float*>(ws);
+  p.keys = pl.key_bytes ? reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + round256(pl.part_bytes))
+                        : nullptr;
+  p.idx = idx;
+  p.maxv = maxv;
+  p.n = (int)m->n;
+  p.k = (int)m->k;
+  p.kb = (int)(m->k / W12_REC_COLS);
+  p.m = (int)M;
+  p.y_f32 = y_dtype == W12_F32;
+  p.mode = op == W12_OP_LMHEAD_ARGMAX ? kModeArgmax : kModeStore;
+  p.fix = fix && m->n_esc > 0;
+  p.q = op == W12_OP_GEMM_Q8;
+  int unsupported = 0;
+  const hipError_t e = launch_gemm(pl, p, reinterpret_cast<hipStream_t>(stream), &unsupported);
+  if (unsupported) return W12_E_M_RANGE;
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return W12_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w12_abi_version(void) { return W12_ABI_VERSION; }
+
+const char* w12_status_str(int status) {
+  switch (status) {
+    case W12_OK: return "ok";
+    case W12_E_INVALID_ARG: return "invalid argument";
+    case W12_E_UNSUPPORTED_SHAPE: return "unsupported shape (need N % 16 == 0, K % 512 == 0)";
+    case W12_E_M_RANGE: return "M out of range (1..64)";
+    case W12_E_WORKSPACE: return "workspace missing or too small";
+    case W12_E_VERSION: return "unsupported format version";
+    case W12_E_HIP: return "HIP runtime error";
+    case W12_E_NOT_IMPLEMENTED: return "not implemented";
+    case W12_E_CORRUPT: return "corrupt descriptor";
+    default: return "unknown status";
+  }
+}
+
+const char* w12_last_error(void) { return g_last_error.c_str(); }
+
+int64_t w12_set_tuning(int key, int64_t value) {
+  int64_t old = 0;
+  if (key == W12_TUNE_PATH) {
+    old = g_tune_path;
+    g_tune_path = (int)value;
+  } else if (key == W12_TUNE_GRID) {
+    old = g_tune_grid;
+    g_tune_grid = value;
+  }
+  return old;
+}
+
+size_t w12_workspace_bytes(int op, int64_t n, int64_t k, int64_t m) {
+  if (check_shape(n, k) != W12_OK) return 0;
+  if (op == W12_OP_ENCODE_PLAN) return round256((size_t)n * sizeof(uint32_t));
+  if (op != W12_OP_GEMM && op != W12_OP_GEMM_Q8 && op != W12_OP_LMHEAD_ARGMAX) return 0;
+  if (m < 1 || m > W12_MAX_M) return 0;
+  return gemm_ws_bytes(make_plan(n, k, m, op));
+}
+
+int w12_encode_plan(const uint16_t* w, int64_t n, int64_t k, uint8_t* e_top, uint32_t* esc_row_ptr,
+                    int64_t* n_esc_host, void* ws, size_t ws_bytes, void* stream) {
+  const int s = check_shape(n, k);
+  if (s != W12_OK) return s;
+  if (!w || !e_top || !esc_row_ptr || !n_esc_host || !aligned16(w)) return W12_E_INVALID_ARG;
+  if (!ws || ws_bytes < (size_t)n * sizeof(uint32_t)) return W12_E_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws);
+  hipError_t e = launch_plan(w, (int)n, (int)k, e_top, cnt, st);
+  if (e != hipSuccess) return hip_fail(e, "encode_plan: window kernel");
+  e = launch_scan(cnt, (int)n, esc_row_ptr, st);
+  if (e != hipSuccess) return hip_fail(e, "encode_plan: scan kernel");
+  uint32_t total = 0;
+  e = hipMemcpyAsync(&total, esc_row_ptr + n, sizeof(uint32_t), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "encode_plan: copy escape count");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "encode_plan: synchronize");
+  *n_esc_host = (int64_t)total;
+  return W12_OK;
+}
+
+int w12_encode(const uint16_t* w, int64_t n, int64_t k, const uint8_t* e_top, const uint32_t* esc_row_ptr,
+               uint8_t* records, w12_escape* esc, void* stream) {
+  const int s = check_shape(n, k);
+  if (s != W12_OK) return s;
+  if (!w || !e_top || !esc_row_ptr || !records || !aligned16(w) || !aligned16(records)) return W12_E_INVALID_ARG;
+  const hipError_t e = launch_pack(w, (int)n, (int)k, e_top, esc_row_ptr, records, esc,
+                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "encode: pack kernel");
+  return W12_OK;
+}
+
+int w12_decode(const w12_matrix* m, uint16_t* w_out, void* stream) {
+  const int s = check_matrix(m);
+  if (s != W12_OK) return s;
+  if (!w_out || !aligned16(w_out)) return W12_E_INVALID_ARG;
+  const hipError_t e = launch_decode(m, w_out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode kernel");
+  return W12_OK;
+}
+
+int w12_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
+             void* ws, size_t ws_bytes, void* stream) {
+  const int s = check_gemm_args(m, x, M, ldx, y, ldy, y_dtype);
+  if (s != W12_OK) return s;
+  return run_gemm(m, x, M, ldx, y, ldy, y_dtype, W12_OP_GEMM, true, ws, ws_bytes, nullptr, nullptr, stream);
+}
+
+int w12_gemm_q8(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,
+                int y_dtype, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  const int s = check_gemm_args(m, x, M, ldx, y, ldy, y_dtype);
+  if (s != W12_OK) return s;
+  if (flags & ~W12_Q8_APPLY_ESCAPES) return W12_E_INVALID_ARG;
+  return run_gemm(m, x, M, ldx, y, ldy, y_dtype, W12_OP_GEMM_Q8, (flags & W12_Q8_APPLY_ESCAPES) != 0, ws,
+                  ws_bytes, nullptr, nullptr, stream);
+}
+
+int w12_lmhead_argmax(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, int32_t* idx,
+                      float* max_logit, void* ws, size_t ws_bytes, void* stream) {
+  const int s = check_gemm_args(m, x, M, ldx, idx, m ? m->n : 0, W12_F32);
+  if (s != W12_OK) return s;
+  return run_gemm(m, x, M, ldx, nullptr, 0, W12_F32, W12_OP_LMHEAD_ARGMAX, true, ws, ws_bytes, idx, max_logit,
+                  stream);
+}
+
+int w12_validate(const w12_matrix* m, void* ws, size_t ws_bytes, void* stream) {
+  const int s = check_matrix(m);
+  if (s != W12_OK) return s;
+  if (!ws || ws_bytes < sizeof(uint32_t)) return W12_E_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* flag = reinterpret_cast<uint32_t*>(ws);
+  hipError_t e = launch_validate(m, flag, st);
+  if (e != hipSuccess) return hip_fail(e, "validate kernel");
+  uint32_t bad = 0;
+  e = hipMemcpyAsync(&bad, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "validate: copy flag");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "validate: synchronize");
+  return bad ? W12_E_CORRUPT : W12_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+// Internal definitions shared by the libw12 translation units: format
+// constants, the in-register decode of W12 records, and kernel launchers.
+//
+// Format (SpecPilot, arXiv 2611.02501, section 4.1 and Figure 5; bit and byte
+// positions as fixed in include/w12.h): a lane that loads the 16 view bytes of
+// one row and 16 consecutive columns (a uint4) and the matching 8 B-plane
+// bytes (a uint2) rebuilds all 16 BF16 weights with three VALU operations per
+// pair of weights.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w12.h"
+
+namespace w12 {
+
+constexpr int kRecRows = W12_REC_ROWS;        // 16
+constexpr int kRecCols = W12_REC_COLS;        // 512
+constexpr int kRecBytes = W12_REC_BYTES;      // 12288
+constexpr int kViewBytes = W12_REC_VIEW_BYTES;  // 8192
+constexpr int kNumCU = 256;                   // MI355X compute units (sizes the stream-K grid)
+
+typedef short short2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// v_perm_b32 selectors over {S0 = view dword, S1 = B dword}: the result holds
+// two 16-bit halves [B byte | view byte] for weights (t, t+1) of the dword.
+constexpr uint32_t kSelPair01 = 0x05010400u;  // bytes B0, V0, B1, V1
+constexpr uint32_t kSelPair23 = 0x07030602u;  // bytes B2, V2, B3, V3
+
+// Arithmetic shift right by 4 of both 16-bit halves (v_pk_ashrrev_i16).
+// A half [v | b] (view byte v high, B byte b low) becomes
+//   bit 15..11 = s, bits 10..7 = off, bits 6..4 = mh, bits 3..0 = high nibble of b.
+__device__ __forceinline__ uint32_t pk_ashr4(uint32_t p) {
+  short2_t s = __builtin_bit_cast(short2_t, p);
+  s = s >> (short2_t){4, 4};
+  return __builtin_bit_cast(uint32_t, s);
+}
+
+// v_bfi_b32: (mask & a) | (~mask & b), one instruction.
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(mask), "v"(a), "v"(b));
+  return d;
+}
+
+// Two weights in the GEMM's scaled domain: the exponent field becomes
+// 112 + off (bits 14..11 forced to 0111), so the pair holds w * 2^(127 - E_n)
+// exactly; the per-row factor 2^(E_n - 127) is applied to the fp32 sum.
+__device__ __forceinline__ uint32_t pair_scaled(uint32_t v, uint32_t b, uint32_t sel, uint32_t c3800) {
+  return bfi(0x78007800u, c3800, pk_ashr4(__builtin_amdgcn_perm(v, b, sel)));
+}
+
+// Two weights with their true exponent off + E_n - 15 (exact decode).
+__device__ __forceinline__ uint32_t pair_exact(uint32_t v, uint32_t b, uint32_t sel, uint32_t bias2) {
+  return (pk_ashr4(__builtin_amdgcn_perm(v, b, sel)) & 0x87FF87FFu) + bias2;
+}
+
+// B dword layout: byte j holds ml(t=j) in its high nibble and ml(t=j+4) in its
+// low nibble, for the 8 weights t = 0..7 the dword covers. Shifting the dword
+// left by 4 moves the low nibbles into the high-nibble positions.
+// In Q mode b0 = b1 = 0x80808080 and no shift is applied: every ml is 1000.
+template <bool kQ>
+__device__ __forceinline__ void decode16_scaled(uint4 v, uint2 b, uint32_t* d, uint32_t c3800) {
+  const uint32_t b0 = kQ ? 0x80808080u : b.x, b1 = kQ ? 0x80808080u : b.y;
+  const uint32_t b0s = kQ ? b0 : (b0 << 4), b1s = kQ ? b1 : (b1 << 4);
+  d[0] = pair_scaled(v.x, b0, kSelPair01, c3800);
+  d[1] = pair_scaled(v.x, b0, kSelPair23, c3800);
+  d[2] = pair_scaled(v.y, b0s, kSelPair01, c3800);
+  d[3] = pair_scaled(v.y, b0s, kSelPair23, c3800);
+  d[4] = pair_scaled(v.z, b1, kSelPair01, c3800);
+  d[5] = pair_scaled(v.z, b1, kSelPair23, c3800);
+  d[6] = pair_scaled(v.w, b1s, kSelPair01, c3800);
+  d[7] = pair_scaled(v.w, b1s, kSelPair23, c3800);
+}
+
+__device__ __forceinline__ void decode16_exact(uint4 v, uint2 b, uint32_t* d, uint32_t bias2) {
+  const uint32_t b0s = b.x << 4, b1s = b.y << 4;
+  d[0] = pair_exact(v.x, b.x, kSelPair01, bias2);
+  d[1] = pair_exact(v.x, b.x, kSelPair23, bias2);
+  d[2] = pair_exact(v.y, b0s, kSelPair01, bias2);
+  d[3] = pair_exact(v.y, b0s, kSelPair23, bias2);
+  d[4] = pair_exact(v.z, b.y, kSelPair01, bias2);
+  d[5] = pair_exact(v.z, b.y, kSelPair23, bias2);
+  d[6] = pair_exact(v.w, b1s, kSelPair01, bias2);
+  d[7] = pair_exact(v.w, b1s, kSelPair23, bias2);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// 2^(E - 127) for E in [1, 254]: an fp32 with exponent field E.
+__device__ __forceinline__ float pow2_scale(uint32_t e_top) { return __uint_as_float(e_top << 23); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Order-preserving 64-bit argmax key: a larger value gives a larger key, and
+// among equal values the lowest index gives the larger key. -0 counts as +0.
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t n) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(0xFFFFFFFFu - n);
+}
+
+__device__ __forceinline__ float key_value(unsigned long long key) {
+  uint32_t u = (uint32_t)(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+
+// Parameters of the GEMM kernels (passed by value).
+struct GemmParams {
+  const uint8_t* rec;
+  const uint8_t* e_top;
+  const uint32_t* row_ptr;
+  const uint2* esc;          // w12_escape as {col, bits | ph << 16}
+  const uint16_t* x;
+  int64_t ldx;
+  void* y;
+  int64_t ldy;
+  float* part;               // partial-sum slots [2P][M][tile_rows]
+  unsigned long long* keys;  // argmax keys [2P][M]
+  int32_t* idx;              // argmax outputs [M]
+  float* maxv;               // argmax values [M] (may be null)
+  int64_t units;             // stream-K work units in the whole matrix
+  int n, k;
+  int kb;                    // records per 16-row block (K / 512)
+  int ku;                    // units per tile
+  int tiles;
+  int P;                     // workgroups
+  int m;                     // activation rows
+  int y_f32;
+  int mode;                  // 0 = store Y, 1 = argmax keys
+  int fix;                   // apply the escape fix-up
+  int q;                     // Q pass (fix-up subtracts the Q view of the placeholder)
+};
+
+enum { kModeStore = 0, kModeArgmax = 1 };
+
+// launchers (return a hipError_t)
+hipError_t launch_plan(const uint16_t* w, int n, int k, uint8_t* e_top, uint32_t* cnt, hipStream_t s);
+hipError_t launch_scan(const uint32_t* cnt, int n, uint32_t* row_ptr, hipStream_t s);
+hipError_t launch_pack(const uint16_t* w, int n, int k, const uint8_t* e_top, const uint32_t* row_ptr,
+                       uint8_t* rec, w12_escape* esc, hipStream_t s);
+hipError_t launch_decode(const w12_matrix* m, uint16_t* out, hipStream_t s);
+hipError_t launch_validate(const w12_matrix* m, uint32_t* flag, hipStream_t s);
+
+struct GemmPlan {
+  bool mfma;
+  int P;
+  int tile_rows;
+  int ku;
+  int tiles;
+  int64_t units;
+  size_t part_bytes;
+  size_t key_bytes;
+};
+GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t grid_override);
+hipError_t launch_gemm(const GemmPlan& plan, GemmParams p, hipStream_t s, int* unsupported);
+
+}  // namespace w12

@@ -1,0 +1,255 @@
+"""Python binding of libw12 (include/w12.h).
+
+Argument marshalling only: every step of encode, decode, GEMM, Q pass and
+argmax runs in the library's HIP kernels. PyTorch provides device memory and
+the current stream. The functions named like the C entry points take and
+return torch tensors; ``encode``/``gemm``/``gemm_q8``/``lmhead_argmax``/
+``decode`` are conveniences that allocate outputs and workspaces.
+
+Importing this module loads libw12.so and fails loudly if it is missing:
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw12.so")
+
+# constants mirrored from include/w12.h
+ABI_VERSION = 1
+FORMAT_VERSION = 1
+REC_ROWS, REC_COLS, REC_BYTES, REC_VIEW_BYTES = 16, 512, 12288, 8192
+MAX_M = 64
+OK, E_INVALID_ARG, E_UNSUPPORTED_SHAPE, E_M_RANGE, E_WORKSPACE, E_VERSION, E_HIP, E_NOT_IMPLEMENTED, E_CORRUPT = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8)
+BF16, F32 = 0, 1
+OP_ENCODE_PLAN, OP_GEMM, OP_GEMM_Q8, OP_LMHEAD_ARGMAX = 1, 2, 3, 4
+Q8_APPLY_ESCAPES = 1
+TUNE_PATH, TUNE_GRID = 1, 2
+
+
+class W12Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = f"{where}: {status_str(status)} ({status})"
+        if status == E_HIP:
+            msg += f": {last_error()}"
+        super().__init__(msg)
+        self.status = status
+
+
+class EscapeC(ctypes.Structure):
+    _fields_ = [("col", ctypes.c_uint32), ("bits", ctypes.c_uint16), ("ph", ctypes.c_uint16)]
+
+
+class MatrixC(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("records", ctypes.c_void_p),
+                ("e_top", ctypes.c_void_p), ("esc_row_ptr", ctypes.c_void_p), ("esc", ctypes.c_void_p),
+                ("n_esc", ctypes.c_int64), ("format_version", ctypes.c_uint32)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_SIGNATURES = {
+    "w12_abi_version": (ctypes.c_int, []),
+    "w12_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "w12_last_error": (ctypes.c_char_p, []),
+    "w12_workspace_bytes": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
+    "w12_encode_plan": (ctypes.c_int, [_P, _I64, _I64, _P, _P, ctypes.POINTER(_I64), _P, _SZ, _P]),
+    "w12_encode": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "w12_decode": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _P]),
+    "w12_gemm": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _SZ, _P]),
+    "w12_gemm_q8": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _I64, ctypes.c_int,
+                                   ctypes.c_uint32, _P, _SZ, _P]),
+    "w12_lmhead_argmax": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "w12_validate": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _SZ, _P]),
+    "w12_set_tuning": (_I64, [ctypes.c_int, _I64]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libw12.so (built by ``lossless_compressed_weight_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m lossless_compressed_weight_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        if handle.w12_abi_version() != ABI_VERSION:
+            raise ImportError("libw12.so ABI version mismatch")
+        _lib = handle
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().w12_status_str(status).decode()
+
+
+def last_error() -> str:
+    return lib().w12_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise W12Error(status, where)
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def set_tuning(key: int, value: int) -> int:
+    return int(lib().w12_set_tuning(key, value))
+
+
+def workspace_bytes(op: int, n: int, k: int, m: int = 0) -> int:
+    return int(lib().w12_workspace_bytes(op, n, k, m))
+
+
+def _workspace(op, n, k, m, device):
+    nb = workspace_bytes(op, n, k, m)
+    return torch.empty(max(nb, 1), dtype=torch.uint8, device=device), nb
+
+
+@dataclass
+class W12Matrix:
+    """An encoded matrix: device tensors plus sizes (format v1)."""
+    n: int
+    k: int
+    records: torch.Tensor   # uint8 [(n/16)(k/512) * 12288]
+    e_top: torch.Tensor     # uint8 [n]
+    row_ptr: torch.Tensor   # int32 [n + 1] (bit pattern of uint32)
+    esc: torch.Tensor       # int64 [n_esc] (bit pattern of the 8-byte entries)
+    n_esc: int
+
+    def desc(self) -> MatrixC:
+        return MatrixC(self.n, self.k, self.records.data_ptr(), self.e_top.data_ptr(), self.row_ptr.data_ptr(),
+                       self.esc.data_ptr() if self.n_esc > 0 else 0, self.n_esc, FORMAT_VERSION)
+
+    @property
+    def device(self):
+        return self.records.device
+
+    def nbytes(self) -> int:
+        return self.records.numel() + self.e_top.numel() + 4 * self.row_ptr.numel() + 8 * self.n_esc
+
+
+def _as_bits16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"expected BF16 data (bfloat16, int16 or uint16 tensor), got {t.dtype}")
+
+
+# ---------------------------------------------------------------- C-named calls
+def w12_encode_plan(w: torch.Tensor, e_top: torch.Tensor, row_ptr: torch.Tensor, ws: torch.Tensor,
+                    stream=None) -> int:
+    n, k = w.shape
+    n_esc = _I64(0)
+    _check(lib().w12_encode_plan(_ptr(w), n, k, _ptr(e_top), _ptr(row_ptr), ctypes.byref(n_esc), _ptr(ws),
+                                 ws.numel(), _stream(stream)), "w12_encode_plan")
+    return int(n_esc.value)
+
+
+def w12_encode(w, e_top, row_ptr, records, esc, stream=None):
+    n, k = w.shape
+    _check(lib().w12_encode(_ptr(w), n, k, _ptr(e_top), _ptr(row_ptr), _ptr(records),
+                            _ptr(esc) if esc is not None and esc.numel() else ctypes.c_void_p(0),
+                            _stream(stream)), "w12_encode")
+
+
+def w12_decode(mat: W12Matrix, out: torch.Tensor, stream=None):
+    d = mat.desc()
+    _check(lib().w12_decode(ctypes.byref(d), _ptr(out), _stream(stream)), "w12_decode")
+
+
+def w12_gemm(mat: W12Matrix, x, y, ws, stream=None):
+    d = mat.desc()
+    ydt = F32 if y.dtype == torch.float32 else BF16
+    _check(lib().w12_gemm(ctypes.byref(d), _ptr(x), x.shape[0], x.stride(0), _ptr(y), y.stride(0), ydt,
+                          _ptr(ws), ws.numel(), _stream(stream)), "w12_gemm")
+
+
+def w12_gemm_q8(mat: W12Matrix, x, y, flags, ws, stream=None):
+    d = mat.desc()
+    ydt = F32 if y.dtype == torch.float32 else BF16
+    _check(lib().w12_gemm_q8(ctypes.byref(d), _ptr(x), x.shape[0], x.stride(0), _ptr(y), y.stride(0), ydt,
+                             flags, _ptr(ws), ws.numel(), _stream(stream)), "w12_gemm_q8")
+
+
+def w12_lmhead_argmax(mat: W12Matrix, x, idx, max_logit, ws, stream=None):
+    d = mat.desc()
+    _check(lib().w12_lmhead_argmax(ctypes.byref(d), _ptr(x), x.shape[0], x.stride(0), _ptr(idx), _ptr(max_logit),
+                                   _ptr(ws), ws.numel(), _stream(stream)), "w12_lmhead_argmax")
+
+
+def w12_validate(mat: W12Matrix, ws: torch.Tensor, stream=None) -> int:
+    d = mat.desc()
+    return int(lib().w12_validate(ctypes.byref(d), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------- conveniences
+def encode(w: torch.Tensor, stream=None) -> W12Matrix:
+    """Encode a BF16 matrix [N, K] that lives on a GPU."""
+    w = _as_bits16(w)
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D tensor")
+    n, k = w.shape
+    dev = w.device
+    e_top = torch.empty(n, dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    ws, _ = _workspace(OP_ENCODE_PLAN, n, k, 0, dev)
+    n_esc = w12_encode_plan(w, e_top, row_ptr, ws, stream)
+    records = torch.empty((n // REC_ROWS) * (k // REC_COLS) * REC_BYTES, dtype=torch.uint8, device=dev)
+    esc = torch.empty(max(n_esc, 1), dtype=torch.int64, device=dev)
+    w12_encode(w, e_top, row_ptr, records, esc if n_esc else None, stream)
+    return W12Matrix(n, k, records, e_top, row_ptr, esc[:n_esc], n_esc)
+
+
+def decode(mat: W12Matrix, stream=None) -> torch.Tensor:
+    out = torch.empty((mat.n, mat.k), dtype=torch.bfloat16, device=mat.device)
+    w12_decode(mat, out, stream)
+    return out
+
+
+def gemm(mat: W12Matrix, x: torch.Tensor, out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    x = _as_bits16(x)
+    y = torch.empty((x.shape[0], mat.n), dtype=out_dtype, device=mat.device)
+    ws, _ = _workspace(OP_GEMM, mat.n, mat.k, x.shape[0], mat.device)
+    w12_gemm(mat, x, y, ws, stream)
+    return y
+
+
+def gemm_q8(mat: W12Matrix, x: torch.Tensor, out_dtype=torch.bfloat16, apply_escapes=False,
+            stream=None) -> torch.Tensor:
+    x = _as_bits16(x)
+    y = torch.empty((x.shape[0], mat.n), dtype=out_dtype, device=mat.device)
+    ws, _ = _workspace(OP_GEMM_Q8, mat.n, mat.k, x.shape[0], mat.device)
+    w12_gemm_q8(mat, x, y, Q8_APPLY_ESCAPES if apply_escapes else 0, ws, stream)
+    return y
+
+
+def lmhead_argmax(mat: W12Matrix, x: torch.Tensor, stream=None):
+    x = _as_bits16(x)
+    m = x.shape[0]
+    idx = torch.empty(m, dtype=torch.int32, device=mat.device)
+    mx = torch.empty(m, dtype=torch.float32, device=mat.device)
+    ws, _ = _workspace(OP_LMHEAD_ARGMAX, mat.n, mat.k, m, mat.device)
+    w12_lmhead_argmax(mat, x, idx, mx, ws, stream)
+    return idx, mx

@@ -1,0 +1,208 @@
+"""GPU GEMM, Q pass and LM-head argmax against the oracle's float64 products.
+
+SpecPilot section 4.1 / Figure 5b (exact W12 GEMM with the escape fix-up and
+a deterministic split of the reduction), section 4.3 (Q pass over the 8-bit
+view with the midpoint rule), Appendix E (W12 LM head; here fused with an
+argmax whose ties go to the lowest index)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import check_bf16, check_f32, dev16, gemm_both, host16, log, o, upload, w12
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _reset_tuning():
+    yield
+    w12.set_tuning(w12.TUNE_PATH, 0)
+    w12.set_tuning(w12.TUNE_GRID, 0)
+
+
+def _mats():
+    return {
+        "config0": synth.workload_matrix(0, 0),                          # 1024 x 1024
+        "ragged_rows": synth.workload_matrix(0, 0)[:48],                  # last GEMV tile has 48 rows
+        "single_record": synth.workload_matrix(0, 0)[:16, :512],
+        "wide_k": synth.workload_matrix(1, 2, rows=slice(0, 256)),       # 256 x 17408
+        "stress": synth.workload_matrix(4, 0, rows=slice(0, 512)),       # ~1% escapes, bimodal rows
+    }
+
+
+MS = [1, 2, 3, 4, 7, 8, 15, 16, 17, 31, 32, 33, 48, 63, 64]
+
+
+@pytest.mark.parametrize("name", list(_mats().keys()))
+@pytest.mark.parametrize("m", MS)
+def test_gemm_matches_fp64_oracle(name, m):
+    w = _mats()[name]
+    log(f"[gemm] {name} {w.shape} M={m}")
+    x = synth.make_activations(m, w.shape[1], seed=1000 + m)
+    mat = w12.encode(dev16(w))
+    yf, yb = gemm_both(mat, dev16(x))
+    y64 = o.gemm_ref(x, w)
+    check_f32(yf, y64, f"{name} M={m}")
+    check_bf16(yb, yf, y64, f"{name} M={m}")
+
+
+@pytest.mark.parametrize("grid", [1, 3, 7, 64, 1000])
+@pytest.mark.parametrize("m", [1, 5, 16, 40])
+def test_split_reduction_any_grid(grid, m):
+    """Every workgroup count splits K differently (partial tiles reduced in a
+    fixed order); all must match the oracle."""
+    w = synth.workload_matrix(0, 0)[:256]
+    x = synth.make_activations(m, 1024, seed=7 + m)
+    mat = w12.encode(dev16(w))
+    w12.set_tuning(w12.TUNE_GRID, grid)
+    yf, yb = gemm_both(mat, dev16(x))
+    check_f32(yf, o.gemm_ref(x, w), f"grid={grid} M={m}")
+
+
+def test_gemv_and_mfma_paths_agree_at_m16():
+    w = synth.workload_matrix(0, 0)
+    x = synth.make_activations(16, 1024, seed=99)
+    mat = w12.encode(dev16(w))
+    y64 = o.gemm_ref(x, w)
+    out = {}
+    for path in (1, 2):
+        w12.set_tuning(w12.TUNE_PATH, path)
+        out[path] = w12.gemm(mat, dev16(x), torch.float32).cpu().numpy()
+        check_f32(out[path], y64, f"path={path}")
+    assert np.max(np.abs(out[1] - out[2]) / np.maximum(np.abs(y64), 1e-3 * np.abs(y64).max())) < 2 * 2e-3
+
+
+def _onehot_case(w, big_scale):
+    enc = o.encode(w)
+    esc_cols = np.unique(enc.esc["col"])
+    cols = np.unique(np.concatenate([[0, 1, 511, 512, w.shape[1] - 1], esc_cols[:40]]))
+    mat = w12.encode(dev16(w))
+    for start in range(0, len(cols), 32):
+        cc = cols[start:start + 32]
+        x = np.zeros((len(cc), w.shape[1]), np.uint16)
+        scale = np.ones(len(cc))
+        for i, c in enumerate(cc):
+            x[i, c] = 0x3F80
+            if big_scale and i % 3 == 0:
+                x[i, c] = 0x4300                                          # 128.0
+                scale[i] = 128.0
+        y = w12.gemm(mat, dev16(x), torch.float32).cpu().numpy()
+        want = scale[:, None] * o.bf16_to_f64(w[:, cc]).T
+        assert np.array_equal(y.astype(np.float64), want), f"cols {cc}"
+
+
+def test_onehot_rows_reproduce_columns_exactly():
+    """x = e_k (or 128 e_k) makes y a column of W: exact, escape columns
+    included (the fix-up removes the placeholder and adds the exact weight)."""
+    _onehot_case(synth.workload_matrix(4, 0, rows=slice(0, 256))[:, :1024], big_scale=True)
+    # every finite BF16 pattern, zeros and subnormals included (x = 1 only: a
+    # larger factor would overflow fp32 on the largest patterns)
+    w = synth.all_bf16_patterns(512).reshape(-1, 1024)
+    w = w[np.isfinite(o.bf16_to_f64(w)).all(axis=1)]
+    _onehot_case(w[: (w.shape[0] // 16) * 16], big_scale=False)
+
+
+def test_deterministic_repeats():
+    w = synth.workload_matrix(4, 0, rows=slice(0, 1024))
+    mat = w12.encode(dev16(w))
+    for m in (1, 8, 32, 64):
+        x = dev16(synth.make_activations(m, w.shape[1], seed=m))
+        a = w12.gemm(mat, x, torch.float32)
+        b = w12.gemm(mat, x, torch.float32)
+        assert torch.equal(a, b)
+        qa = w12.gemm_q8(mat, x, torch.float32)
+        qb = w12.gemm_q8(mat, x, torch.float32)
+        assert torch.equal(qa, qb)
+
+
+def test_strided_activations_and_outputs():
+    w = synth.workload_matrix(0, 0)
+    mat = w12.encode(dev16(w))
+    for m in (3, 20):
+        xfull = synth.make_activations(m, 1024 + 64, seed=m)
+        xd = dev16(xfull)[:, :1024]                                       # ldx = 1088
+        y = torch.full((m, 1024 + 32), -7.0, dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, w12.workspace_bytes(w12.OP_GEMM, 1024, 1024, m)), dtype=torch.uint8, device="cuda")
+        w12.w12_gemm(mat, xd, y[:, :1024], ws)
+        yh = y.cpu().numpy()
+        check_f32(yh[:, :1024], o.gemm_ref(xfull[:, :1024], w), f"strided M={m}")
+        assert np.all(yh[:, 1024:] == -7.0)                               # nothing written past N
+
+
+@pytest.mark.parametrize("m", [1, 8, 16, 32])
+def test_q8_matches_oracle_view(m):
+    w = synth.workload_matrix(4, 0, rows=slice(0, 512))
+    enc = o.encode(w)
+    x = synth.make_activations(m, w.shape[1], seed=300 + m)
+    mat = w12.encode(dev16(w))
+    yf, yb = gemm_both(mat, dev16(x), q=True)
+    yq64 = o.gemm_q8_ref(x, enc)
+    check_f32(yf, yq64, f"Q M={m}")
+    check_bf16(yb, yf, yq64, f"Q M={m}")
+    # with escapes applied the Q pass differs from the Q view only at escapes
+    yfe, _ = gemm_both(mat, dev16(x), q=True, apply_escapes=True)
+    qbits = o.q_view_bits(enc)
+    rows = np.repeat(np.arange(enc.n), np.diff(enc.row_ptr.astype(np.int64)))
+    qbits[rows, enc.esc["col"].astype(np.int64)] = enc.esc["bits"]
+    check_f32(yfe, o.gemm_ref(x, qbits), f"Q+escapes M={m}")
+
+
+def test_q8_equals_exact_when_low_bits_are_midpoint():
+    w = (synth.plain_gaussian(256, 1024, seed=12) & 0xFFF0) | 0x0008
+    enc = o.encode(w)
+    keep = np.ones(w.shape[0], bool)
+    rows = np.repeat(np.arange(enc.n), np.diff(enc.row_ptr.astype(np.int64)))
+    keep[rows] = False                                                   # rows without escapes
+    w = w[keep][: (keep.sum() // 16) * 16]
+    assert o.encode(w).n_esc == 0
+    mat = w12.encode(dev16(w))
+    for m in (1, 32):
+        x = dev16(synth.make_activations(m, 1024, seed=m))
+        assert torch.equal(w12.gemm(mat, x, torch.float32), w12.gemm_q8(mat, x, torch.float32))
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 32, 64])
+def test_lmhead_argmax_small(m):
+    rng = np.random.default_rng(m)
+    w = synth.workload_matrix(3, 0, rows=slice(0, 2048))
+    x = synth.make_activations(m, w.shape[1], seed=500 + m)
+    mat = w12.encode(dev16(w))
+    idx, mx = w12.lmhead_argmax(mat, dev16(x))
+    yf = w12.gemm(mat, dev16(x), torch.float32).cpu().numpy()
+    idx = idx.cpu().numpy()
+    mx = mx.cpu().numpy()
+    # the fused argmax is the argmax of the same kernel's fp32 logits
+    assert np.array_equal(idx, np.argmax(yf, axis=1))
+    assert np.array_equal(mx, yf[np.arange(m), idx])
+    # and the oracle's, away from near-ties
+    ridx, margin = o.argmax_ref(o.gemm_ref(x, w))
+    far = margin >= 1e-3
+    assert np.array_equal(idx[far], ridx[far])
+    del rng
+
+
+def test_lmhead_argmax_planted_ties_and_negatives():
+    """All-negative logits, exact ties (lowest index wins) and -0 vs +0."""
+    k = 512
+    w = np.zeros((64, k), np.uint16)
+    w[:, 0] = 0xBF80                                                     # every logit = -x0
+    w[10, 0] = 0xBF00                                                    # -0.5: the max for x0 > 0
+    w[40, 0] = 0xBF00                                                    # tie with row 10
+    mat = w12.encode(dev16(w))
+    x = np.zeros((2, k), np.uint16)
+    x[0, 0] = 0x4000                                                     # 2.0
+    x[1, 0] = 0x0000                                                     # all logits +-0 -> row 0
+    idx, mx = w12.lmhead_argmax(mat, dev16(x))
+    assert idx.cpu().tolist() == [10, 0]
+    assert mx.cpu().tolist() == [-1.0, 0.0]
+
+
+def test_oracle_encoded_records_drive_the_gemm():
+    """The GEMM reads the oracle's bytes as well as the GPU encoder's."""
+    w = synth.workload_matrix(0, 0)
+    x = synth.make_activations(32, 1024, seed=4)
+    y_gpu_enc = w12.gemm(w12.encode(dev16(w)), dev16(x), torch.float32)
+    y_orc_enc = w12.gemm(upload(o.encode(w)), dev16(x), torch.float32)
+    assert torch.equal(y_gpu_enc, y_orc_enc)
+    log(f"max |y| {float(y_gpu_enc.abs().max()):.3f}; bits {host16(y_gpu_enc.to(torch.bfloat16))[0, :2]}")
