@@ -84,8 +84,7 @@ def main():
             n, k = w.shape
             x = torch.from_numpy(xs_host[m][:, :k].copy().view(np.int16)).to(dev)
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-            nb = w12.workspace_bytes(w12.OP_GEMM, n, k, m)
-            ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+            ws = w12.new_workspace(w12.OP_GEMM, n, k, m, dev)
             calls.append((m, i, x, y, ws))
     stream = torch.cuda.current_stream()
 

@@ -56,8 +56,12 @@
  * - Results are deterministic: the same inputs and shape give the same bits
  *   (the K reduction is split over workgroups in a fixed order that depends
  *   only on N, K and M).
- * - Concurrent calls need distinct workspaces. Workspaces need no
- *   initialisation and hold nothing between calls.
+ * - Concurrent calls need distinct workspaces. The first W12_WS_COUNTER_BYTES
+ *   of a GEMM workspace (W12_OP_GEMM, _GEMM_Q8, _LMHEAD_ARGMAX) are counter
+ *   words that must be zero before the workspace's first use (allocate it
+ *   zero-filled once); every call leaves them zero again, so one workspace
+ *   serves any sequence of GEMM calls, ops, matrices and sizes that fit in
+ *   it. The rest of a workspace carries nothing from one call to the next.
  * - W12_E_HIP: a HIP call failed; w12_last_error() names it (thread-local).
  */
 #ifndef W12_H
@@ -78,6 +82,7 @@ extern "C" {
 #define W12_REC_BYTES 12288
 #define W12_REC_VIEW_BYTES 8192
 #define W12_MAX_M 64
+#define W12_WS_COUNTER_BYTES 16640 /* counter words at the start of a GEMM workspace */
 
 /* status codes */
 #define W12_OK 0
@@ -182,7 +187,8 @@ int w12_validate(const w12_matrix* m, void* ws, size_t ws_bytes, void* stream);
 /* Test and tuning hooks (process-wide, not thread-safe; call before launching).
  * W12_TUNE_PATH: 0 = choose by M, 1 = force the GEMV kernel (M <= 15 only is
  *   the default range; forcing allows up to 16), 2 = force the MFMA kernel.
- * W12_TUNE_GRID: workgroup count for the GEMM kernels (0 = default).
+ * W12_TUNE_GRID: workgroup count for the GEMM kernels (0 = default; at most
+ *   4096 and at most the number of work units are used).
  * Changing W12_TUNE_GRID changes the fp32 summation order and the workspace
  * size; query w12_workspace_bytes after setting it. Returns the old value. */
 #define W12_TUNE_PATH 1

@@ -55,7 +55,10 @@ int check_gemm_args(const w12_matrix* m, const void* x, int64_t M, int64_t ldx, 
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-size_t gemm_ws_bytes(const GemmPlan& pl) { return round256(pl.part_bytes) + round256(pl.key_bytes); }
+// workspace: [counters | partial slots | argmax keys], each 256-byte aligned
+size_t gemm_ws_bytes(const GemmPlan& pl) {
+  return round256(pl.ctr_bytes) + round256(pl.part_bytes) + round256(pl.key_bytes);
+}
 
 GemmPlan make_plan(int64_t n, int64_t k, int64_t M, int op) {
   return plan_gemm(n, k, M, op, g_tune_path, g_tune_grid);
@@ -76,8 +79,10 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   p.ldx = ldx;
   p.y = y;
   p.ldy = ldy;
-  p.part = reinterpret_cast<float*>(ws);
-  p.keys = pl.key_bytes ? reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + round256(pl.part_bytes))
+  char* wsb = reinterpret_cast<char*>(ws);
+  p.ctr = reinterpret_cast<uint32_t*>(wsb);
+  p.part = reinterpret_cast<float*>(wsb + round256(pl.ctr_bytes));
+  p.keys = pl.key_bytes ? reinterpret_cast<unsigned long long*>(wsb + round256(pl.ctr_bytes) + round256(pl.part_bytes))
                         : nullptr;
   p.idx = idx;
   p.maxv = maxv;

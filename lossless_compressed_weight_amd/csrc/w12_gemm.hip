@@ -6,20 +6,33 @@
 // are deterministic. Section 4.3: the Q pass reads only the 8-bit view.
 // Appendix E: the LM head in W12, here fused with a per-row argmax.
 //
-// Work decomposition (both kernels): the matrix is a sequence of tiles of rows
+// Work decomposition (both kernels): the matrix is a sequence of row tiles
 // (64 rows for the GEMV kernel, 16 for the MFMA kernel), each a sequence of
-// units along K (128 columns for GEMV, 256 for MFMA: one pipeline stage of
-// every wave of a workgroup, so trip counts are exact). Workgroup p owns the
-// contiguous unit range [p U / P, (p+1) U / P). A tile covered by one
-// workgroup is finished there (per-row scale, escape fix-up, output); a tile
-// split between workgroups leaves fp32 partial sums in fixed slots (2p for a
-// workgroup's first tile, 2p+1 for its last), which k_reduce adds in workgroup
-// order.
+// units of 256 columns along K (one pipeline stage for each of a workgroup's
+// four waves, so trip counts are exact). Workgroup p owns the contiguous unit
+// range [p U / P, (p+1) U / P).
+//
+// A segment (the units of one tile that a workgroup owns) yields, per output
+// row and activation row, A = sum of x * w' over its columns, where w' is the
+// weight decoded with a fixed exponent bias (w = w' 2^(E_n - 127)), plus the
+// escape corrections of its columns: CN = sum of x * placeholder and CP = sum
+// of x * exact escape value. The segment's value is (A 2^(E_n-127) - CN) + CP.
+// The corrections are gathered at the start of the segment, while its first
+// weight loads are in flight, so finishing a segment needs no global loads.
+//
+// A tile covered by one workgroup is finished there. A tile split between
+// workgroups: each stores its segment value in a fixed slot (2p for a
+// workgroup's first tile, 2p+1 for its last) and counts itself in the tile's
+// counter; the last to arrive adds the slots in workgroup order (so the result
+// does not depend on arrival order) and writes the tile. Counters wrap back to
+// zero, so every call leaves them zeroed for the next one.
 #include "w12_internal.h"
 
 namespace w12 {
 
-// -------------------------------------------------------------- shared pieces
+constexpr int kUnitCols = 256;
+
+// -------------------------------------------------------------- stream-K map
 __device__ __forceinline__ int64_t unit_start(int64_t p, int64_t units, int P) { return p * units / P; }
 
 // Workgroup owning unit u.
@@ -27,24 +40,18 @@ __device__ __forceinline__ int unit_owner(int64_t u, int64_t units, int P) {
   return (int)(((u + 1) * P + units - 1) / units) - 1;
 }
 
-// Scale, escape fix-up, then either store y[m, n] or fold the value into the
-// workgroup's argmax key for row m.
-__device__ __forceinline__ void finish_value(const GemmParams& a, int n, int m, float s,
-                                             unsigned long long* kbest) {
+__device__ __forceinline__ bool wg_empty(int q, const GemmParams& a) {
+  return unit_start(q, a.units, a.P) == unit_start(q + 1, a.units, a.P);
+}
+
+// Slot of workgroup q's segment of tile t.
+__device__ __forceinline__ int tile_slot(int q, int64_t t, const GemmParams& a) {
+  return (unit_start(q, a.units, a.P) / a.ku == t) ? 2 * q : 2 * q + 1;
+}
+
+// -------------------------------------------------------------- outputs
+__device__ __forceinline__ void emit(const GemmParams& a, int n, int m, float v, unsigned long long* kbest) {
   if (n >= a.n) return;
-  float v = s * pow2_scale(a.e_top[n]);
-  if (a.fix) {
-    const uint16_t* xr = a.x + (int64_t)m * a.ldx;
-    const uint32_t e0 = a.row_ptr[n], e1 = a.row_ptr[n + 1];
-    for (uint32_t i = e0; i < e1; ++i) {
-      const uint2 e = a.esc[i];
-      const float xv = bf16_to_f32(xr[e.x]);
-      uint32_t ph = e.y >> 16;
-      if (a.q) ph = (ph & 0xFFF0u) | 0x8u;
-      v = fmaf(-xv, bf16_to_f32(ph), v);
-      v = fmaf(xv, bf16_to_f32(e.y & 0xFFFFu), v);
-    }
-  }
   if (a.mode == kModeStore) {
     if (a.y_f32) reinterpret_cast<float*>(a.y)[(int64_t)m * a.ldy + n] = v;
     else reinterpret_cast<uint16_t*>(a.y)[(int64_t)m * a.ldy + n] = f32_to_bf16_rne(v);
@@ -53,61 +60,170 @@ __device__ __forceinline__ void finish_value(const GemmParams& a, int n, int m, 
   }
 }
 
+// Cross-workgroup exchange without an L2 writeback: segment values and keys
+// are written and read with agent-scope atomic stores and loads (coherent
+// across the XCDs' separate L2 caches); each thread waits until its own
+// stores are acknowledged, then one thread counts the workgroup in.
+__device__ __forceinline__ void store_shared(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long load_shared(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Count this workgroup into counter c (n arrivals in all; the counter wraps to
+// 0 on the last). Returns, to every thread, whether this workgroup was last.
+__device__ __forceinline__ bool arrive(uint32_t* c, uint32_t n, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's coherent stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __builtin_amdgcn_atomic_inc32(c, n - 1, __ATOMIC_RELAXED, "agent");
+    *flag = old == n - 1;
+  }
+  __syncthreads();
+  return *flag;
+}
+
+// Finish segment values value(m, row) of tile t (tile_rows rows from output
+// row row0): written directly for a whole tile, through the slots and the
+// tile counter for a split one.
+template <class ValFn>
+__device__ __forceinline__ void finish_segment(const GemmParams& a, int64_t t, int tile_rows, int row0, bool whole,
+                                               int p, ValFn value, unsigned long long* kbest, int* flag) {
+  const int nval = a.m * tile_rows;
+  if (whole) {
+    for (int i = threadIdx.x; i < nval; i += blockDim.x) {
+      const int m = i / tile_rows, row = i % tile_rows;
+      emit(a, row0 + row, m, value(m, row), kbest);
+    }
+    return;
+  }
+  float* dst = a.part + (int64_t)tile_slot(p, t, a) * a.m * tile_rows;
+  for (int i = threadIdx.x; i < nval; i += blockDim.x) {
+    const int m = i / tile_rows, row = i % tile_rows;
+    store_shared(&dst[m * tile_rows + row], value(m, row));
+  }
+  const int64_t u_first = t * a.ku, u_last = min(a.units, (t + 1) * a.ku) - 1;
+  const int pa = unit_owner(u_first, a.units, a.P), pb = unit_owner(u_last, a.units, a.P);
+  uint32_t c = 0;
+  for (int q = pa; q <= pb; ++q) c += !wg_empty(q, a);
+  // a workgroup owns the first unit of at most one split tile, so the owner's
+  // index names the tile's counter
+  if (arrive(&a.ctr[pa], c, flag)) {
+    for (int i = threadIdx.x; i < nval; i += blockDim.x) {
+      const int m = i / tile_rows, row = i % tile_rows;
+      float v = 0.f;
+      for (int q = pa; q <= pb; ++q) {
+        if (wg_empty(q, a)) continue;
+        v += load_shared(&a.part[((int64_t)tile_slot(q, t, a) * a.m + m) * tile_rows + row]);
+      }
+      emit(a, row0 + row, m, v, kbest);
+    }
+  }
+  __syncthreads();
+}
+
+// Argmax mode: publish this workgroup's best key per activation row; the last
+// workgroup to finish reduces all of them into idx / max.
+__device__ __forceinline__ void finish_argmax(const GemmParams& a, int p, unsigned long long* kbest, int* flag) {
+  __syncthreads();
+  if (threadIdx.x < a.m) store_shared(&a.keys[(int64_t)p * a.m + threadIdx.x], kbest[threadIdx.x]);
+  if (arrive(&a.ctr[kMaxGrid], (uint32_t)a.P, flag)) {
+    if (threadIdx.x < a.m) {
+      unsigned long long best = 0ull;
+      for (int q = 0; q < a.P; ++q) {
+        const unsigned long long k = load_shared(&a.keys[(int64_t)q * a.m + threadIdx.x]);
+        best = k > best ? k : best;
+      }
+      a.idx[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+      if (a.maxv) a.maxv[threadIdx.x] = key_value(best);
+    }
+  }
+}
+
+// -------------------------------------------------------------- escapes
+// First escape of row n with column >= c0 (binary search in the row's
+// column-sorted list), and the end of the row's list.
+__device__ __forceinline__ uint32_t esc_lower_bound(const GemmParams& a, int n, uint32_t c0, uint32_t* end) {
+  uint32_t lo = a.row_ptr[n], hi = a.row_ptr[n + 1];
+  *end = hi;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (a.esc[mid].x < c0) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// The weight the main loop used for an escape: its placeholder, seen through
+// the Q view (low nibble 1000) in the Q pass.
+__device__ __forceinline__ float esc_placeholder(const GemmParams& a, uint32_t packed) {
+  uint32_t ph = packed >> 16;
+  if (a.q) ph = (ph & 0xFFF0u) | 0x8u;
+  return bf16_to_f32(ph);
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t w, uint32_t x, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, x), acc,
                                          false);
 }
 
 // Software pipeline over the units [u, ue) of one segment with two register
-// stages: the loads of the next unit are in flight while the current one is
-// computed. All loads are unconditional (the prefetch past the last unit
-// re-reads the last unit and is never used), so the compiler can count them
-// with vmcnt across the loop.
-template <class Stage, class Load, class Compute>
-__device__ __forceinline__ void pipeline(int u, int ue, Load&& load, Compute&& compute) {
-  if (u >= ue) return;
+// stages: the loads of unit u+1 are in flight while unit u is computed. mid()
+// runs once after the first two stages are issued. All loads are
+// unconditional (a prefetch past the last unit re-reads it and is unused), so
+// the compiler can count them with vmcnt across the loop.
+template <class Stage, class Load, class Compute, class Mid>
+__device__ __forceinline__ void pipeline(int u, int ue, Load&& load, Compute&& compute, Mid&& mid) {
   Stage sa, sb;
   load(sa, u);
+  load(sb, min(u + 1, ue - 1));
+  mid();
+  __builtin_amdgcn_sched_barrier(0);
   for (;;) {
-    load(sb, min(u + 1, ue - 1));
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
     compute(sa);
     if (++u == ue) break;
     load(sa, min(u + 1, ue - 1));
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
     compute(sb);
     if (++u == ue) break;
+    load(sb, min(u + 1, ue - 1));
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // ============================================================== GEMV (M < 16)
 // A wave covers 64 rows (lane = row, four 16-row blocks) and one 16-column
-// group per step: each lane loads 16 view bytes and 8 B-plane bytes of its own
-// row, rebuilds 16 weights and accumulates M dot products. The activations of
-// a step are the same for all lanes, so they come through scalar loads and
-// feed v_dot2c_f32_bf16 as its SGPR operand; no cross-lane reduction is needed.
-// A unit is 8 column groups (128 columns); wave w takes groups w and w + 4.
-// The four waves' sums are added through LDS in wave order.
+// group per step: each lane loads the 16 view bytes and 8 B-plane bytes of its
+// own row, rebuilds 16 weights and accumulates M dot products. The activations
+// of a step are the same for every lane, so they come through scalar loads and
+// feed v_dot2c_f32_bf16 as its SGPR operand; no cross-lane reduction is
+// needed. In a unit (16 groups) wave w takes groups w, w+4, w+8, w+12; the
+// four waves' sums are added through LDS in wave order.
 constexpr int kGemvTileRows = 64;
-constexpr int kGemvUnitCols = 128;
+constexpr int kGemvSteps = 4;  // column groups per wave per unit
 
-// Activations are prefetched into SGPRs with the weights when they fit
-// (M <= 4); otherwise they are read right before use.
 template <int M>
-constexpr bool kGemvPrefetchX = M <= 4;
+constexpr bool kGemvPrefetchX = M == 1;
 
 template <int M, bool Q>
 struct GemvStage {
-  uint4 v[2];
-  uint2 b[2];
+  uint4 v[kGemvSteps];
+  uint2 b[kGemvSteps];
   int g;
-  uint32_t x[kGemvPrefetchX<M> ? 2 : 1][kGemvPrefetchX<M> ? M : 1][8];
+  uint32_t x[kGemvPrefetchX<M> ? kGemvSteps : 1][8];
 };
 
 template <int M, bool Q>
 __global__ __launch_bounds__(256) void k_gemv(GemmParams a, const uint16_t* __restrict__ x) {
-  __shared__ float red[4 * M * kGemvTileRows];
+  __shared__ float red[3][4][M][kGemvTileRows];  // A, CN, CP per wave
   __shared__ unsigned long long kbest[M];
+  __shared__ int flag;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x;
@@ -115,40 +231,37 @@ __global__ __launch_bounds__(256) void k_gemv(GemmParams a, const uint16_t* __re
   const uint32_t c3800 = 0x38003800u;
   const int64_t ldx = a.ldx;
   if (threadIdx.x < M) kbest[threadIdx.x] = 0ull;
-  const int first_tile = (int)(u0 / a.ku);
   for (int64_t u = u0; u < u1;) {
     const int tile = (int)(u / a.ku);
     const int k0 = (int)(u - (int64_t)tile * a.ku);
     const int k1 = (int)min((int64_t)a.ku, u1 - (int64_t)tile * a.ku);
-    // lane -> row: block tile*4 + lane/16, row lane%16; rows past N read block 0
-    const bool ok = (tile * 4 + (lane >> 4)) * kRecRows < a.n;
+    // lane -> row tile*64 + lane; rows past N read block 0 of the tile
+    const int row = tile * kGemvTileRows + lane;
+    const bool ok = row < a.n;
     const uint8_t* tile_rec = a.rec + (int64_t)tile * 4 * a.kb * kRecBytes;
     const uint32_t soff = ok ? (uint32_t)(lane >> 4) * (uint32_t)(a.kb * kRecBytes) : 0u;
     const uint32_t voff = soff + (lane & 15) * 16, boff = soff + kViewBytes + (lane & 15) * 8;
-    float acc[M];
+    float acc[M], cn[M], cp[M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.f;
+    for (int m = 0; m < M; ++m) acc[m] = cn[m] = cp[m] = 0.f;
     auto load = [&](GemvStage<M, Q>& st, int kk) {
-      st.g = kk * 8 + wave;
+      st.g = kk * 16 + wave;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kGemvSteps; ++j) {
         const int gj = st.g + 4 * j;
         const uint32_t sb = (uint32_t)(gj >> 5) * kRecBytes;
         st.v[j] = *reinterpret_cast<const uint4*>(tile_rec + (sb + (gj & 31) * 256 + voff));
         if (!Q) st.b[j] = *reinterpret_cast<const uint2*>(tile_rec + (sb + (gj & 31) * 128 + boff));
         if constexpr (kGemvPrefetchX<M>) {
+          const uint32_t* xp = reinterpret_cast<const uint32_t*>(x + gj * 16);
 #pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const uint32_t* xp = reinterpret_cast<const uint32_t*>(x + (int64_t)m * ldx + gj * 16);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) st.x[j][m][t] = xp[t];
-          }
+          for (int t = 0; t < 8; ++t) st.x[j][t] = xp[t];
         }
       }
     };
     auto compute = [&](const GemvStage<M, Q>& st) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kGemvSteps; ++j) {
         const int gj = st.g + 4 * j;
         uint32_t d[8];
         decode16_scaled<Q>(st.v[j], Q ? make_uint2(0, 0) : st.b[j], d, c3800);
@@ -157,35 +270,57 @@ __global__ __launch_bounds__(256) void k_gemv(GemmParams a, const uint16_t* __re
           const uint32_t* xp = reinterpret_cast<const uint32_t*>(x + (int64_t)m * ldx + gj * 16);
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
-            const uint32_t xv = kGemvPrefetchX<M> ? st.x[kGemvPrefetchX<M> ? j : 0][kGemvPrefetchX<M> ? m : 0][t]
-                                                  : xp[t];
+            const uint32_t xv = kGemvPrefetchX<M> ? st.x[kGemvPrefetchX<M> ? j : 0][t] : xp[t];
             acc[m] = dot2_bf16(d[t], xv, acc[m]);
           }
         }
       }
     };
-    pipeline<GemvStage<M, Q>>(k0, k1, load, compute);
+    // escape corrections of this lane's row in this wave's column groups
+    auto corrections = [&]() {
+      if (!a.fix || !ok) return;
+      uint32_t end;
+      const uint32_t c0 = (uint32_t)k0 * kUnitCols, c1 = (uint32_t)k1 * kUnitCols;
+      for (uint32_t i = esc_lower_bound(a, row, c0, &end); i < end; ++i) {
+        const uint2 e = a.esc[i];
+        if (e.x >= c1) break;
+        if (((e.x >> 4) & 3u) != (uint32_t)wave) continue;
+        const float ph = esc_placeholder(a, e.y), ex = bf16_to_f32(e.y & 0xFFFFu);
 #pragma unroll
-    for (int m = 0; m < M; ++m) red[(wave * M + m) * kGemvTileRows + lane] = acc[m];
-    __syncthreads();
-    const bool whole = (k0 == 0 && k1 == a.ku);
-    const int slot = (tile == first_tile) ? 2 * p : 2 * p + 1;
-    for (int i = threadIdx.x; i < M * kGemvTileRows; i += 256) {
-      const int m = i / kGemvTileRows, row = i % kGemvTileRows;
-      float s = red[(0 * M + m) * kGemvTileRows + row];
-      s += red[(1 * M + m) * kGemvTileRows + row];
-      s += red[(2 * M + m) * kGemvTileRows + row];
-      s += red[(3 * M + m) * kGemvTileRows + row];
-      if (whole) finish_value(a, tile * kGemvTileRows + row, m, s, kbest);
-      else a.part[((int64_t)slot * M + m) * kGemvTileRows + row] = s;
+        for (int m = 0; m < M; ++m) {
+          const float xv = bf16_to_f32(x[(int64_t)m * ldx + e.x]);
+          cn[m] = fmaf(xv, ph, cn[m]);
+          cp[m] = fmaf(xv, ex, cp[m]);
+        }
+      }
+    };
+    pipeline<GemvStage<M, Q>>(k0, k1, load, compute, corrections);
+    const float scale = pow2_scale(a.e_top[ok ? row : 0]);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      red[0][wave][m][lane] = acc[m];
+      red[1][wave][m][lane] = cn[m];
+      red[2][wave][m][lane] = cp[m];
     }
+    __syncthreads();
+    // thread (wave w, lane l) finishes rows l for m = w, w+4, ...: its scale is its own row's
+    auto value = [&](int m, int r) {
+      const float s = (r == lane) ? scale : pow2_scale(a.e_top[min(tile * kGemvTileRows + r, a.n - 1)]);
+      float A = red[0][0][m][r], CN = red[1][0][m][r], CP = red[2][0][m][r];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        A += red[0][w][m][r];
+        CN += red[1][w][m][r];
+        CP += red[2][w][m][r];
+      }
+      return (A * s - CN) + CP;
+    };
+    const bool whole = (k0 == 0 && k1 == a.ku);
+    finish_segment(a, tile, kGemvTileRows, tile * kGemvTileRows, whole, p, value, kbest, &flag);
     __syncthreads();
     u = (int64_t)tile * a.ku + k1;
   }
-  if (a.mode == kModeArgmax) {
-    __syncthreads();
-    if (threadIdx.x < M) a.keys[(int64_t)p * M + threadIdx.x] = kbest[threadIdx.x];
-  }
+  if (a.mode == kModeArgmax) finish_argmax(a, p, kbest, &flag);
 }
 
 // ============================================================== MFMA (M >= 16)
@@ -197,9 +332,12 @@ __global__ __launch_bounds__(256) void k_gemv(GemmParams a, const uint16_t* __re
 // A unit is 4 chunks (256 columns); wave w takes chunk w. Whole 16-row blocks
 // are processed R at a time so one activation load serves R blocks. The four
 // waves' sums are added through LDS in wave order.
-constexpr int kMfmaR = 4;
+// Blocks per group: 4 up to two m-tiles; 2 beyond, which keeps the kernel's
+// registers within the architectural VGPRs (with four blocks and four m-tiles
+// the compiler's register assignment produced wrong results).
+template <int MT>
+constexpr int kMfmaR = MT <= 2 ? 4 : 2;
 constexpr int kMfmaTileRows = 16;
-constexpr int kMfmaUnitCols = 256;
 
 template <int MT, int RG, bool Q>
 struct MfmaStage {
@@ -208,26 +346,33 @@ struct MfmaStage {
   uint2 b[RG];
 };
 
+template <int MT>
+struct MfmaShared {
+  float red[4][kMfmaR<MT>][MT][4][64];    // per wave: C of each block and m-tile
+  float cn[kMfmaR<MT> * 16][MT * 16];     // escape corrections per (row, m)
+  float cp[kMfmaR<MT> * 16][MT * 16];
+  float scale[kMfmaR<MT> * 16];
+};
+
 // One group: RG consecutive 16-row blocks starting at block s, units [k0, k1).
 template <int MT, int RG, bool Q>
 __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, int k1, int wave, int lane,
-                                           float* red) {
+                                           MfmaShared<MT>& sh) {
   f32x4_t acc[RG][MT];
 #pragma unroll
   for (int j = 0; j < RG; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[j][mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const uint32_t c3800 = 0x38003800u;
-  // activation row mt*16 + lane%16 (row 0 and a zero operand past M), columns
-  // 16 (lane/16) + 0..15 of the chunk: per-lane byte offsets from the chunk
-  uint32_t ok_mask = 0;
+  // activation row mt*16 + lane%16, columns 16 (lane/16) + 0..15 of the chunk:
+  // per-lane byte offsets from the chunk. Past M the lane reads row 0: those
+  // B columns only feed output columns m >= M, which are never stored, so the
+  // loads need no predicate.
   uint32_t xoff[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int row = mt * 16 + (lane & 15);
-    const bool ok = row < a.m;
-    ok_mask |= ok ? (1u << mt) : 0u;
-    xoff[mt] = (uint32_t)((ok ? row : 0) * a.ldx + (lane >> 4) * 16) * 2u;
+    xoff[mt] = (uint32_t)((row < a.m ? row : 0) * a.ldx + (lane >> 4) * 16) * 2u;
   }
   const uint8_t* blk = a.rec + (int64_t)s * a.kb * kRecBytes;
   const uint32_t blk_stride = (uint32_t)(a.kb * kRecBytes);
@@ -237,10 +382,8 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint4* xp = reinterpret_cast<const uint4*>(xc + xoff[mt]);
-      const uint4 x0 = xp[0], x1 = xp[1];
-      const bool ok = (ok_mask >> mt) & 1u;
-      st.x[mt][0] = ok ? x0 : make_uint4(0, 0, 0, 0);
-      st.x[mt][1] = ok ? x1 : make_uint4(0, 0, 0, 0);
+      st.x[mt][0] = xp[0];
+      st.x[mt][1] = xp[1];
     }
     const uint32_t rec_off = (uint32_t)(c >> 3) * kRecBytes;
 #pragma unroll
@@ -268,112 +411,88 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
       }
     }
   };
-  pipeline<MfmaStage<MT, RG, Q>>(k0, k1, load, compute);
+  // per-row scale and escape corrections of the group's columns, one thread
+  // per (row, activation row) pair
+  auto mid = [&]() {
+    const int rows = RG * 16;
+    if (threadIdx.x < rows) sh.scale[threadIdx.x] = pow2_scale(a.e_top[s * 16 + threadIdx.x]);
+    const uint32_t c0 = (uint32_t)k0 * kUnitCols, c1 = (uint32_t)k1 * kUnitCols;
+    for (int q = threadIdx.x; q < rows * a.m; q += 256) {
+      const int rr = q % rows, m = q / rows;
+      float cn = 0.f, cp = 0.f;
+      if (a.fix) {
+        uint32_t end;
+        const uint16_t* xr = a.x + (int64_t)m * a.ldx;
+        for (uint32_t i = esc_lower_bound(a, s * 16 + rr, c0, &end); i < end; ++i) {
+          const uint2 e = a.esc[i];
+          if (e.x >= c1) break;
+          const float xv = bf16_to_f32(xr[e.x]);
+          cn = fmaf(xv, esc_placeholder(a, e.y), cn);
+          cp = fmaf(xv, bf16_to_f32(e.y & 0xFFFFu), cp);
+        }
+      }
+      sh.cn[rr][m] = cn;
+      sh.cp[rr][m] = cp;
+    }
+  };
+  pipeline<MfmaStage<MT, RG, Q>>(k0, k1, load, compute, mid);
   // C layout of a 16x16 MFMA: lane l holds rows 4 (l/16) + i, column l % 16.
 #pragma unroll
   for (int j = 0; j < RG; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[(((wave * kMfmaR + j) * MT + mt) * 4 + i) * 64 + lane] = acc[j][mt][i];
+      for (int i = 0; i < 4; ++i) sh.red[wave][j][mt][i][lane] = acc[j][mt][i];
 }
 
 template <int MT, bool Q>
 __global__ __launch_bounds__(256) void k_mfma(GemmParams a) {
-  __shared__ float red[4 * kMfmaR * MT * 4 * 64];
+  __shared__ MfmaShared<MT> sh;
   __shared__ unsigned long long kbest[MT * 16];
+  __shared__ int flag;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x;
   const int64_t u0 = unit_start(p, a.units, a.P), u1 = unit_start(p + 1, a.units, a.P);
   if (threadIdx.x < MT * 16) kbest[threadIdx.x] = 0ull;
-  const int first_tile = (int)(u0 / a.ku);
   for (int64_t u = u0; u < u1;) {
     const int s = (int)(u / a.ku);
     const int k0 = (int)(u - (int64_t)s * a.ku);
     int rg, k1;
     if (k0 == 0 && (int64_t)(s + 1) * a.ku <= u1) {
-      rg = (int)min((int64_t)kMfmaR, (u1 - u) / a.ku);
+      rg = (int)min((int64_t)kMfmaR<MT>, (u1 - u) / a.ku);
       k1 = a.ku;
     } else {
       rg = 1;
       k1 = (int)min((int64_t)a.ku, u1 - (int64_t)s * a.ku);
     }
-    switch (rg) {
-      case 1: mfma_group<MT, 1, Q>(a, s, k0, k1, wave, lane, red); break;
-      case 2: mfma_group<MT, 2, Q>(a, s, k0, k1, wave, lane, red); break;
-      case 3: mfma_group<MT, 3, Q>(a, s, k0, k1, wave, lane, red); break;
-      default: mfma_group<MT, 4, Q>(a, s, k0, k1, wave, lane, red); break;
+    if constexpr (kMfmaR<MT> == 4) {
+      switch (rg) {
+        case 1: mfma_group<MT, 1, Q>(a, s, k0, k1, wave, lane, sh); break;
+        case 2: mfma_group<MT, 2, Q>(a, s, k0, k1, wave, lane, sh); break;
+        case 3: mfma_group<MT, 3, Q>(a, s, k0, k1, wave, lane, sh); break;
+        default: mfma_group<MT, 4, Q>(a, s, k0, k1, wave, lane, sh); break;
+      }
+    } else {
+      if (rg == 1) mfma_group<MT, 1, Q>(a, s, k0, k1, wave, lane, sh);
+      else mfma_group<MT, 2, Q>(a, s, k0, k1, wave, lane, sh);
     }
     __syncthreads();
     const bool whole = (k0 == 0 && k1 == a.ku);
-    const int slot = (s == first_tile) ? 2 * p : 2 * p + 1;
-    const int rows = rg * 16;
-    for (int q = threadIdx.x; q < rows * a.m; q += 256) {
-      const int m = q / rows, rr = q % rows;
+    // C of block j at (row, m): lane (row/4)*16 + m%16, element row%4, m-tile m/16
+    auto value = [&](int m, int rr) {
       const int j = rr >> 4, row = rr & 15;
       const int mt = m >> 4, l = (row >> 2) * 16 + (m & 15), i = row & 3;
-      float v = 0.f;
+      float A = sh.red[0][j][mt][i][l];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v += red[(((w * kMfmaR + j) * MT + mt) * 4 + i) * 64 + l];
-      if (whole) finish_value(a, (s + j) * 16 + row, m, v, kbest);
-      else a.part[((int64_t)slot * a.m + m) * kMfmaTileRows + row] = v;
-    }
+      for (int w = 1; w < 4; ++w) A += sh.red[w][j][mt][i][l];
+      return (A * sh.scale[rr] - sh.cn[rr][m]) + sh.cp[rr][m];
+    };
+    finish_segment(a, s, rg * kMfmaTileRows, s * kMfmaTileRows, whole, p, value, kbest, &flag);
     __syncthreads();
     u = (int64_t)(s + rg - 1) * a.ku + k1;
   }
-  if (a.mode == kModeArgmax) {
-    __syncthreads();
-    if (threadIdx.x < a.m) a.keys[(int64_t)p * a.m + threadIdx.x] = kbest[threadIdx.x];
-  }
-}
-
-// ============================================================== reduce / finalize
-// Block b (boundary between workgroups b-1 and b, b = 1..P-1): if that boundary
-// falls inside a tile and is the first boundary in it, sum the tile's partial
-// slots in workgroup order and finish it.
-__global__ __launch_bounds__(256) void k_reduce(GemmParams a, int tile_rows) {
-  __shared__ unsigned long long kbest[W12_MAX_M];
-  const int b = blockIdx.x + 1;
-  if (threadIdx.x < a.m) kbest[threadIdx.x] = 0ull;
-  __syncthreads();
-  const int64_t ub = unit_start(b, a.units, a.P);
-  const int64_t t = ub / a.ku;
-  const bool mine = b < a.P && ub < a.units && (ub % a.ku) != 0 &&
-                    unit_start(b - 1, a.units, a.P) <= t * a.ku;
-  if (mine) {
-    const int pa = unit_owner(t * a.ku, a.units, a.P);
-    const int pb = unit_owner(min(a.units, (t + 1) * a.ku) - 1, a.units, a.P);
-    for (int q = threadIdx.x; q < tile_rows * a.m; q += blockDim.x) {
-      const int m = q / tile_rows, row = q % tile_rows;
-      float v = 0.f;
-      for (int pp = pa; pp <= pb; ++pp) {
-        const int64_t sp = unit_start(pp, a.units, a.P);
-        if (sp == unit_start(pp + 1, a.units, a.P)) continue;
-        const int slot = (sp / a.ku == t) ? 2 * pp : 2 * pp + 1;
-        v += a.part[((int64_t)slot * a.m + m) * tile_rows + row];
-      }
-      finish_value(a, (int)(t * tile_rows) + row, m, v, kbest);
-    }
-  }
-  if (a.mode == kModeArgmax) {
-    __syncthreads();
-    if (threadIdx.x < a.m) a.keys[((int64_t)a.P + blockIdx.x) * a.m + threadIdx.x] = kbest[threadIdx.x];
-  }
-}
-
-__global__ __launch_bounds__(64) void k_argmax_final(const unsigned long long* __restrict__ keys, int nslots,
-                                                     int m, int32_t* __restrict__ idx,
-                                                     float* __restrict__ maxv) {
-  const int i = threadIdx.x;
-  if (i >= m) return;
-  unsigned long long best = 0ull;
-  for (int s = 0; s < nslots; ++s) {
-    const unsigned long long k = keys[(int64_t)s * m + i];
-    best = k > best ? k : best;
-  }
-  idx[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
-  if (maxv) maxv[i] = key_value(best);
+  if (a.mode == kModeArgmax) finish_argmax(a, p, kbest, &flag);
 }
 
 // ============================================================== planning
@@ -382,28 +501,30 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t gr
   pl.mfma = (path == 2) || (path == 0 && m >= 16);
   if (pl.mfma) {
     pl.tile_rows = kMfmaTileRows;
-    pl.ku = (int)(k / kMfmaUnitCols);
+    pl.ku = (int)(k / kUnitCols);
     pl.tiles = (int)(n / 16);
   } else {
     pl.tile_rows = kGemvTileRows;
-    pl.ku = (int)(k / kGemvUnitCols);
+    pl.ku = (int)(k / kUnitCols);
     pl.tiles = (int)((n + kGemvTileRows - 1) / kGemvTileRows);
   }
   pl.units = (int64_t)pl.tiles * pl.ku;
   // One resident round of workgroups (occupancy set by the kernels' register
   // and LDS use); at least a few units per workgroup.
   const int64_t mt = (m + 15) / 16;
-  const int64_t per_cu = pl.mfma ? (mt == 1 ? 4 : (mt == 2 ? 2 : 1)) : 4;
+  const int64_t per_cu = pl.mfma ? (mt == 1 ? 4 : 2) : 4;
   int64_t P = kNumCU * per_cu;
-  const int64_t min_units = pl.mfma ? 4 : 8;
+  const int64_t min_units = 2;
   if (pl.units / min_units < P) P = pl.units / min_units;
   if (grid_override > 0) P = grid_override;
+  if (P > kMaxGrid) P = kMaxGrid;
   if (P > pl.units) P = pl.units;
   if (P < 1) P = 1;
   pl.P = (int)P;
   const int64_t mm = pl.mfma ? ((m + 15) / 16) * 16 : m;
+  pl.ctr_bytes = kCounterBytes;
   pl.part_bytes = (size_t)(2 * P) * (size_t)mm * pl.tile_rows * sizeof(float);
-  pl.key_bytes = (op == W12_OP_LMHEAD_ARGMAX) ? (size_t)(2 * P) * (size_t)m * 8 : 0;
+  pl.key_bytes = (op == W12_OP_LMHEAD_ARGMAX) ? (size_t)P * (size_t)m * 8 : 0;
   return pl;
 }
 
@@ -435,15 +556,6 @@ static hipError_t launch_mfma_m(const GemmPlan& pl, const GemmParams& p, hipStre
   return hipGetLastError();
 }
 
-// True if some boundary between workgroups falls inside a tile.
-static bool has_split_tiles(const GemmPlan& pl) {
-  for (int64_t b = 1; b < pl.P; ++b) {
-    const int64_t ub = b * pl.units / pl.P;
-    if (ub % pl.ku != 0) return true;
-  }
-  return false;
-}
-
 hipError_t launch_gemm(const GemmPlan& pl, GemmParams p, hipStream_t s, int* unsupported) {
   *unsupported = 0;
   p.units = pl.units;
@@ -454,22 +566,8 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmParams p, hipStream_t s, int* uns
     *unsupported = 1;
     return hipSuccess;
   }
-  hipError_t e = pl.mfma ? (p.q ? launch_mfma_m<true>(pl, p, s) : launch_mfma_m<false>(pl, p, s))
-                         : (p.q ? launch_gemv_m<true>(pl, p, s) : launch_gemv_m<false>(pl, p, s));
-  if (e != hipSuccess) return e;
-  if (p.mode == kModeArgmax || has_split_tiles(pl)) {
-    if (pl.P > 1) {
-      hipLaunchKernelGGL(k_reduce, dim3(pl.P - 1), dim3(256), 0, s, p, pl.tile_rows);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  if (p.mode == kModeArgmax) {
-    const int nslots = pl.P + (pl.P - 1);
-    hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(64), 0, s, p.keys, nslots, p.m, p.idx, p.maxv);
-    e = hipGetLastError();
-  }
-  return e;
+  return pl.mfma ? (p.q ? launch_mfma_m<true>(pl, p, s) : launch_mfma_m<false>(pl, p, s))
+                 : (p.q ? launch_gemv_m<true>(pl, p, s) : launch_gemv_m<false>(pl, p, s));
 }
 
 }  // namespace w12

@@ -20,6 +20,12 @@ constexpr int kRecCols = W12_REC_COLS;        // 512
 constexpr int kRecBytes = W12_REC_BYTES;      // 12288
 constexpr int kViewBytes = W12_REC_VIEW_BYTES;  // 8192
 constexpr int kNumCU = 256;                   // MI355X compute units (sizes the stream-K grid)
+constexpr int kMaxGrid = 4096;                // most workgroups a GEMM launch uses
+// Counter words at the start of every GEMM workspace: one per workgroup (the
+// split tile whose first unit it owns) plus the argmax completion counter.
+// Same size and place for every op and shape, and zero between calls.
+constexpr size_t kCounterBytes = W12_WS_COUNTER_BYTES;
+static_assert(kCounterBytes >= (kMaxGrid + 1) * sizeof(uint32_t), "counter region too small");
 
 typedef short short2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -122,8 +128,9 @@ struct GemmParams {
   int64_t ldx;
   void* y;
   int64_t ldy;
+  uint32_t* ctr;             // split-tile counters [tiles], then the argmax counter; zero between calls
   float* part;               // partial-sum slots [2P][M][tile_rows]
-  unsigned long long* keys;  // argmax keys [2P][M]
+  unsigned long long* keys;  // per-workgroup argmax keys [P][M]
   int32_t* idx;              // argmax outputs [M]
   float* maxv;               // argmax values [M] (may be null)
   int64_t units;             // stream-K work units in the whole matrix
@@ -156,6 +163,7 @@ struct GemmPlan {
   int ku;
   int tiles;
   int64_t units;
+  size_t ctr_bytes;
   size_t part_bytes;
   size_t key_bytes;
 };

@@ -25,6 +25,7 @@ ABI_VERSION = 1
 FORMAT_VERSION = 1
 REC_ROWS, REC_COLS, REC_BYTES, REC_VIEW_BYTES = 16, 512, 12288, 8192
 MAX_M = 64
+WS_COUNTER_BYTES = 16640
 OK, E_INVALID_ARG, E_UNSUPPORTED_SHAPE, E_M_RANGE, E_WORKSPACE, E_VERSION, E_HIP, E_NOT_IMPLEMENTED, E_CORRUPT = (
     0, -1, -2, -3, -4, -5, -6, -7, -8)
 BF16, F32 = 0, 1
@@ -123,9 +124,16 @@ def workspace_bytes(op: int, n: int, k: int, m: int = 0) -> int:
     return int(lib().w12_workspace_bytes(op, n, k, m))
 
 
-def _workspace(op, n, k, m, device):
+def new_workspace(op: int, n: int, k: int, m: int = 0, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for `op` (the GEMM ops need their counter words
+    zero before the first call; every call leaves them zero again)."""
     nb = workspace_bytes(op, n, k, m)
-    return torch.empty(max(nb, 1), dtype=torch.uint8, device=device), nb
+    return torch.zeros(max(nb, 1), dtype=torch.uint8, device=device)
+
+
+def _workspace(op, n, k, m, device):
+    ws = new_workspace(op, n, k, m, device)
+    return ws, ws.numel()
 
 
 @dataclass

@@ -103,6 +103,34 @@ def test_onehot_rows_reproduce_columns_exactly():
     _onehot_case(w[: (w.shape[0] // 16) * 16], big_scale=False)
 
 
+@pytest.mark.parametrize("grid", [0, 5, 333])
+def test_workspace_reuse_across_calls(grid):
+    """Split tiles count their workgroups in the workspace and reset the count:
+    one workspace serves many calls, ops and sizes in a row."""
+    w12.set_tuning(w12.TUNE_GRID, grid)
+    w = synth.workload_matrix(0, 0)
+    mat = w12.encode(dev16(w))
+    big = max(w12.workspace_bytes(op, 1024, 1024, m) for op in (w12.OP_GEMM, w12.OP_GEMM_Q8, w12.OP_LMHEAD_ARGMAX)
+              for m in (1, 7, 16, 33, 64))
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    ref = o.encode(w)
+    for rep in range(3):
+        for m in (1, 7, 16, 33, 64):
+            x = synth.make_activations(m, 1024, seed=rep * 100 + m)
+            y = torch.empty((m, 1024), dtype=torch.float32, device="cuda")
+            w12.w12_gemm(mat, dev16(x), y, ws)
+            check_f32(y.cpu().numpy(), o.gemm_ref(x, w), f"reuse grid={grid} rep={rep} M={m}")
+            w12.w12_gemm_q8(mat, dev16(x), y, 0, ws)
+            check_f32(y.cpu().numpy(), o.gemm_q8_ref(x, ref), f"reuse Q grid={grid} rep={rep} M={m}")
+            idx = torch.empty(m, dtype=torch.int32, device="cuda")
+            w12.w12_lmhead_argmax(mat, dev16(x), idx, None, ws)
+            ridx, margin = o.argmax_ref(o.gemm_ref(x, w))
+            far = margin >= 1e-3
+            assert np.array_equal(idx.cpu().numpy()[far], ridx[far])
+    torch.cuda.synchronize()
+    assert int(ws[: w12.WS_COUNTER_BYTES].view(torch.int32).abs().sum()) == 0   # counters back at zero
+
+
 def test_deterministic_repeats():
     w = synth.workload_matrix(4, 0, rows=slice(0, 1024))
     mat = w12.encode(dev16(w))
@@ -123,7 +151,7 @@ def test_strided_activations_and_outputs():
         xfull = synth.make_activations(m, 1024 + 64, seed=m)
         xd = dev16(xfull)[:, :1024]                                       # ldx = 1088
         y = torch.full((m, 1024 + 32), -7.0, dtype=torch.float32, device="cuda")
-        ws = torch.empty(max(1, w12.workspace_bytes(w12.OP_GEMM, 1024, 1024, m)), dtype=torch.uint8, device="cuda")
+        ws = w12.new_workspace(w12.OP_GEMM, 1024, 1024, m)
         w12.w12_gemm(mat, xd, y[:, :1024], ws)
         yh = y.cpu().numpy()
         check_f32(yh[:, :1024], o.gemm_ref(xfull[:, :1024], w), f"strided M={m}")
