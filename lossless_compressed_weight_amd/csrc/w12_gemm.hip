@@ -17,8 +17,8 @@
 // weight decoded with a fixed exponent bias (w = w' 2^(E_n - 127)), plus the
 // escape corrections of its columns: CN = sum of x * placeholder and CP = sum
 // of x * exact escape value. The segment's value is (A 2^(E_n-127) - CN) + CP.
-// The corrections are gathered at the start of the segment, while its first
-// weight loads are in flight, so finishing a segment needs no global loads.
+// The scales and corrections are gathered by a helper wave while the
+// streaming waves run, so finishing a segment needs no global loads.
 //
 // A tile covered by one workgroup is finished there. A tile split between
 // workgroups: each stores its segment value in a fixed slot (2p for a
@@ -174,27 +174,26 @@ __device__ __forceinline__ float dot2_bf16(uint32_t w, uint32_t x, float acc) {
 }
 
 // Software pipeline over the units [u, ue) of one segment with two register
-// stages: the loads of unit u+1 are in flight while unit u is computed. mid()
-// runs once after the first two stages are issued. All loads are
-// unconditional (a prefetch past the last unit re-reads it and is unused), so
-// the compiler can count them with vmcnt across the loop.
-template <class Stage, class Load, class Compute, class Mid>
-__device__ __forceinline__ void pipeline(int u, int ue, Load&& load, Compute&& compute, Mid&& mid) {
+// stages: the loads of unit u+1 are in flight while unit u is computed. All
+// loads are unconditional (a prefetch past the last unit re-reads it and is
+// unused) and nothing with a data-dependent number of loads runs between
+// them, so the compiler's vmcnt waits stay exact and the prefetch overlaps.
+template <class Stage, class Load, class Compute>
+__device__ __forceinline__ void pipeline(int u, int ue, Load&& load, Compute&& compute) {
+  // Loop invariant: at the top, only stage a's loads (unit u + i) are in flight.
   Stage sa, sb;
   load(sa, u);
-  load(sb, min(u + 1, ue - 1));
-  mid();
-  __builtin_amdgcn_sched_barrier(0);
-  for (;;) {
-    compute(sa);
-    if (++u == ue) break;
-    load(sa, min(u + 1, ue - 1));
+  const int n = ue - u;
+  int i = 0;
+  for (; i + 2 <= n; i += 2) {
+    load(sb, u + i + 1);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-    compute(sb);
-    if (++u == ue) break;
-    load(sb, min(u + 1, ue - 1));
+    compute(sa);
+    load(sa, min(u + i + 2, ue - 1));
     __builtin_amdgcn_sched_barrier(0);
+    compute(sb);
   }
+  if (i < n) compute(sa);
 }
 
 // ============================================================== GEMV (M < 16)
@@ -203,32 +202,43 @@ __device__ __forceinline__ void pipeline(int u, int ue, Load&& load, Compute&& c
 // own row, rebuilds 16 weights and accumulates M dot products. The activations
 // of a step are the same for every lane, so they come through scalar loads and
 // feed v_dot2c_f32_bf16 as its SGPR operand; no cross-lane reduction is
-// needed. In a unit (16 groups) wave w takes groups w, w+4, w+8, w+12; the
-// four waves' sums are added through LDS in wave order.
+// needed. In a unit (16 groups) streaming wave w takes groups w, w+4, w+8,
+// w+12; the four waves' sums are added through LDS in wave order.
+//
+// Both kernels run a fifth, helper wave beside the four streaming ones: it
+// reads the per-row scales and gathers the escape corrections of the
+// segment's columns (irregular, latency-bound work with its own wait
+// counters), so the streaming waves never stall on it.
 constexpr int kGemvTileRows = 64;
 constexpr int kGemvSteps = 4;  // column groups per wave per unit
-
-template <int M>
-constexpr bool kGemvPrefetchX = M == 1;
+constexpr int kStreamWaves = 4;
+constexpr int kThreads = (kStreamWaves + 1) * 64;
 
 template <int M, bool Q>
 struct GemvStage {
   uint4 v[kGemvSteps];
   uint2 b[kGemvSteps];
   int g;
-  uint32_t x[kGemvPrefetchX<M> ? kGemvSteps : 1][8];
+};
+
+template <int M>
+struct GemvShared {
+  float acc[kStreamWaves][M][kGemvTileRows];
+  float cn[M][kGemvTileRows];
+  float cp[M][kGemvTileRows];
+  float scale[kGemvTileRows];
 };
 
 template <int M, bool Q>
-__global__ __launch_bounds__(256) void k_gemv(GemmParams a, const uint16_t* __restrict__ x) {
-  __shared__ float red[3][4][M][kGemvTileRows];  // A, CN, CP per wave
+__global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t* __restrict__ x) {
+  __shared__ GemvShared<M> sh;
   __shared__ unsigned long long kbest[M];
   __shared__ int flag;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x;
   const int64_t u0 = unit_start(p, a.units, a.P), u1 = unit_start(p + 1, a.units, a.P);
-  const uint32_t c3800 = 0x38003800u;
+  const uint32_t c3800 = opaque_vgpr(0x38003800u);
   const int64_t ldx = a.ldx;
   if (threadIdx.x < M) kbest[threadIdx.x] = 0ull;
   for (int64_t u = u0; u < u1;) {
@@ -238,82 +248,74 @@ __global__ __launch_bounds__(256) void k_gemv(GemmParams a, const uint16_t* __re
     // lane -> row tile*64 + lane; rows past N read block 0 of the tile
     const int row = tile * kGemvTileRows + lane;
     const bool ok = row < a.n;
-    const uint8_t* tile_rec = a.rec + (int64_t)tile * 4 * a.kb * kRecBytes;
-    const uint32_t soff = ok ? (uint32_t)(lane >> 4) * (uint32_t)(a.kb * kRecBytes) : 0u;
-    const uint32_t voff = soff + (lane & 15) * 16, boff = soff + kViewBytes + (lane & 15) * 8;
-    float acc[M], cn[M], cp[M];
+    if (wave < kStreamWaves) {
+      const uint8_t* tile_rec = a.rec + (int64_t)tile * 4 * a.kb * kRecBytes;
+      const uint32_t soff = ok ? (uint32_t)(lane >> 4) * (uint32_t)(a.kb * kRecBytes) : 0u;
+      const uint32_t voff = soff + (lane & 15) * 16, boff = soff + kViewBytes + (lane & 15) * 8;
+      float acc[M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = cn[m] = cp[m] = 0.f;
-    auto load = [&](GemvStage<M, Q>& st, int kk) {
-      st.g = kk * 16 + wave;
+      for (int m = 0; m < M; ++m) acc[m] = 0.f;
+      auto load = [&](GemvStage<M, Q>& st, int kk) {
+        st.g = kk * 16 + wave;
 #pragma unroll
-      for (int j = 0; j < kGemvSteps; ++j) {
-        const int gj = st.g + 4 * j;
-        const uint32_t sb = (uint32_t)(gj >> 5) * kRecBytes;
-        st.v[j] = *reinterpret_cast<const uint4*>(tile_rec + (sb + (gj & 31) * 256 + voff));
-        if (!Q) st.b[j] = *reinterpret_cast<const uint2*>(tile_rec + (sb + (gj & 31) * 128 + boff));
-        if constexpr (kGemvPrefetchX<M>) {
-          const uint32_t* xp = reinterpret_cast<const uint32_t*>(x + gj * 16);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) st.x[j][t] = xp[t];
+        for (int j = 0; j < kGemvSteps; ++j) {
+          const int gj = st.g + 4 * j;
+          const uint32_t sb = (uint32_t)(gj >> 5) * kRecBytes;
+          st.v[j] = *reinterpret_cast<const uint4*>(tile_rec + (sb + (gj & 31) * 256 + voff));
+          if (!Q) st.b[j] = *reinterpret_cast<const uint2*>(tile_rec + (sb + (gj & 31) * 128 + boff));
         }
-      }
-    };
-    auto compute = [&](const GemvStage<M, Q>& st) {
+      };
+      auto compute = [&](const GemvStage<M, Q>& st) {
 #pragma unroll
-      for (int j = 0; j < kGemvSteps; ++j) {
-        const int gj = st.g + 4 * j;
-        uint32_t d[8];
-        decode16_scaled<Q>(st.v[j], Q ? make_uint2(0, 0) : st.b[j], d, c3800);
+        for (int j = 0; j < kGemvSteps; ++j) {
+          const int gj = st.g + 4 * j;
+          uint32_t d[8];
+          decode16_scaled<Q>(st.v[j], Q ? make_uint2(0, 0) : st.b[j], d, c3800);
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const uint32_t* xp = reinterpret_cast<const uint32_t*>(x + (int64_t)m * ldx + gj * 16);
+          for (int m = 0; m < M; ++m) {
+            const uint32_t* xp = reinterpret_cast<const uint32_t*>(x + (int64_t)m * ldx + gj * 16);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const uint32_t xv = kGemvPrefetchX<M> ? st.x[kGemvPrefetchX<M> ? j : 0][t] : xp[t];
-            acc[m] = dot2_bf16(d[t], xv, acc[m]);
+            for (int t = 0; t < 8; ++t) acc[m] = dot2_bf16(d[t], xp[t], acc[m]);
+          }
+        }
+      };
+      pipeline<GemvStage<M, Q>>(k0, k1, load, compute);
+#pragma unroll
+      for (int m = 0; m < M; ++m) sh.acc[wave][m][lane] = acc[m];
+    } else {
+      // helper: scale and escape corrections of this lane's row over the
+      // segment's columns, in column order
+      float cn[M], cp[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) cn[m] = cp[m] = 0.f;
+      if (a.fix && ok) {
+        uint32_t end;
+        const uint32_t c0 = (uint32_t)k0 * kUnitCols, c1 = (uint32_t)k1 * kUnitCols;
+        for (uint32_t i = esc_lower_bound(a, row, c0, &end); i < end; ++i) {
+          const uint2 e = a.esc[i];
+          if (e.x >= c1) break;
+          const float ph = esc_placeholder(a, e.y), ex = bf16_to_f32(e.y & 0xFFFFu);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            const float xv = bf16_to_f32(x[(int64_t)m * ldx + e.x]);
+            cn[m] = fmaf(xv, ph, cn[m]);
+            cp[m] = fmaf(xv, ex, cp[m]);
           }
         }
       }
-    };
-    // escape corrections of this lane's row in this wave's column groups
-    auto corrections = [&]() {
-      if (!a.fix || !ok) return;
-      uint32_t end;
-      const uint32_t c0 = (uint32_t)k0 * kUnitCols, c1 = (uint32_t)k1 * kUnitCols;
-      for (uint32_t i = esc_lower_bound(a, row, c0, &end); i < end; ++i) {
-        const uint2 e = a.esc[i];
-        if (e.x >= c1) break;
-        if (((e.x >> 4) & 3u) != (uint32_t)wave) continue;
-        const float ph = esc_placeholder(a, e.y), ex = bf16_to_f32(e.y & 0xFFFFu);
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const float xv = bf16_to_f32(x[(int64_t)m * ldx + e.x]);
-          cn[m] = fmaf(xv, ph, cn[m]);
-          cp[m] = fmaf(xv, ex, cp[m]);
-        }
+      for (int m = 0; m < M; ++m) {
+        sh.cn[m][lane] = cn[m];
+        sh.cp[m][lane] = cp[m];
       }
-    };
-    pipeline<GemvStage<M, Q>>(k0, k1, load, compute, corrections);
-    const float scale = pow2_scale(a.e_top[ok ? row : 0]);
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      red[0][wave][m][lane] = acc[m];
-      red[1][wave][m][lane] = cn[m];
-      red[2][wave][m][lane] = cp[m];
+      sh.scale[lane] = pow2_scale(a.e_top[ok ? row : 0]);
     }
     __syncthreads();
-    // thread (wave w, lane l) finishes rows l for m = w, w+4, ...: its scale is its own row's
     auto value = [&](int m, int r) {
-      const float s = (r == lane) ? scale : pow2_scale(a.e_top[min(tile * kGemvTileRows + r, a.n - 1)]);
-      float A = red[0][0][m][r], CN = red[1][0][m][r], CP = red[2][0][m][r];
+      float A = sh.acc[0][m][r];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        A += red[0][w][m][r];
-        CN += red[1][w][m][r];
-        CP += red[2][w][m][r];
-      }
-      return (A * s - CN) + CP;
+      for (int w = 1; w < kStreamWaves; ++w) A += sh.acc[w][m][r];
+      return (A * sh.scale[r] - sh.cn[m][r]) + sh.cp[m][r];
     };
     const bool whole = (k0 == 0 && k1 == a.ku);
     finish_segment(a, tile, kGemvTileRows, tile * kGemvTileRows, whole, p, value, kbest, &flag);
@@ -329,15 +331,17 @@ __global__ __launch_bounds__(256) void k_gemv(GemmParams a, const uint16_t* __re
 // global memory. A wave's 1 KB view load of one 64-column chunk of a 16-row
 // block gives lane l row l%16 and columns 16 (l/16) .. +15: exactly the A
 // operands of two MFMAs; the B operands use the same lane -> column map.
-// A unit is 4 chunks (256 columns); wave w takes chunk w. Whole 16-row blocks
-// are processed R at a time so one activation load serves R blocks. The four
-// waves' sums are added through LDS in wave order.
+// A unit is 4 chunks (256 columns); streaming wave w takes chunk w. Whole
+// 16-row blocks are processed R at a time so one activation load serves R
+// blocks. The four waves' sums are added through LDS in wave order; the
+// helper wave gathers scales and escape corrections meanwhile.
+constexpr int kMfmaTileRows = 16;
+
 // Blocks per group: 4 up to two m-tiles; 2 beyond, which keeps the kernel's
 // registers within the architectural VGPRs (with four blocks and four m-tiles
 // the compiler's register assignment produced wrong results).
 template <int MT>
 constexpr int kMfmaR = MT <= 2 ? 4 : 2;
-constexpr int kMfmaTileRows = 16;
 
 template <int MT, int RG, bool Q>
 struct MfmaStage {
@@ -348,8 +352,8 @@ struct MfmaStage {
 
 template <int MT>
 struct MfmaShared {
-  float red[4][kMfmaR<MT>][MT][4][64];    // per wave: C of each block and m-tile
-  float cn[kMfmaR<MT> * 16][MT * 16];     // escape corrections per (row, m)
+  float red[kStreamWaves][kMfmaR<MT>][MT][4][64];  // per wave: C of each block and m-tile
+  float cn[kMfmaR<MT> * 16][MT * 16];              // escape corrections per (row, m)
   float cp[kMfmaR<MT> * 16][MT * 16];
   float scale[kMfmaR<MT> * 16];
 };
@@ -358,12 +362,47 @@ struct MfmaShared {
 template <int MT, int RG, bool Q>
 __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, int k1, int wave, int lane,
                                            MfmaShared<MT>& sh) {
+  if (wave == kStreamWaves) {
+    // helper: lane = row of the group; escape corrections for every m, in
+    // column order, sixteen activation rows at a time
+    const int rows = RG * 16;
+    if (lane < rows) {
+      const int n = s * 16 + lane;
+      sh.scale[lane] = pow2_scale(a.e_top[n]);
+      const uint32_t c0 = (uint32_t)k0 * kUnitCols, c1 = (uint32_t)k1 * kUnitCols;
+      uint32_t end = 0, first = 0;
+      if (a.fix) first = esc_lower_bound(a, n, c0, &end);
+      for (int m0 = 0; m0 < a.m; m0 += 16) {
+        float cn[16], cp[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) cn[j] = cp[j] = 0.f;
+        for (uint32_t i = first; i < end; ++i) {
+          const uint2 e = a.esc[i];
+          if (e.x >= c1) break;
+          const float ph = esc_placeholder(a, e.y), ex = bf16_to_f32(e.y & 0xFFFFu);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int m = min(m0 + j, a.m - 1);
+            const float xv = bf16_to_f32(a.x[(int64_t)m * a.ldx + e.x]);
+            cn[j] = fmaf(xv, ph, cn[j]);
+            cp[j] = fmaf(xv, ex, cp[j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          sh.cn[lane][m0 + j] = cn[j];
+          sh.cp[lane][m0 + j] = cp[j];
+        }
+      }
+    }
+    return;
+  }
   f32x4_t acc[RG][MT];
 #pragma unroll
   for (int j = 0; j < RG; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[j][mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  const uint32_t c3800 = 0x38003800u;
+  const uint32_t c3800 = opaque_vgpr(0x38003800u);
   // activation row mt*16 + lane%16, columns 16 (lane/16) + 0..15 of the chunk:
   // per-lane byte offsets from the chunk. Past M the lane reads row 0: those
   // B columns only feed output columns m >= M, which are never stored, so the
@@ -411,31 +450,7 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
       }
     }
   };
-  // per-row scale and escape corrections of the group's columns, one thread
-  // per (row, activation row) pair
-  auto mid = [&]() {
-    const int rows = RG * 16;
-    if (threadIdx.x < rows) sh.scale[threadIdx.x] = pow2_scale(a.e_top[s * 16 + threadIdx.x]);
-    const uint32_t c0 = (uint32_t)k0 * kUnitCols, c1 = (uint32_t)k1 * kUnitCols;
-    for (int q = threadIdx.x; q < rows * a.m; q += 256) {
-      const int rr = q % rows, m = q / rows;
-      float cn = 0.f, cp = 0.f;
-      if (a.fix) {
-        uint32_t end;
-        const uint16_t* xr = a.x + (int64_t)m * a.ldx;
-        for (uint32_t i = esc_lower_bound(a, s * 16 + rr, c0, &end); i < end; ++i) {
-          const uint2 e = a.esc[i];
-          if (e.x >= c1) break;
-          const float xv = bf16_to_f32(xr[e.x]);
-          cn = fmaf(xv, esc_placeholder(a, e.y), cn);
-          cp = fmaf(xv, bf16_to_f32(e.y & 0xFFFFu), cp);
-        }
-      }
-      sh.cn[rr][m] = cn;
-      sh.cp[rr][m] = cp;
-    }
-  };
-  pipeline<MfmaStage<MT, RG, Q>>(k0, k1, load, compute, mid);
+  pipeline<MfmaStage<MT, RG, Q>>(k0, k1, load, compute);
   // C layout of a 16x16 MFMA: lane l holds rows 4 (l/16) + i, column l % 16.
 #pragma unroll
   for (int j = 0; j < RG; ++j)
@@ -446,7 +461,7 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
 }
 
 template <int MT, bool Q>
-__global__ __launch_bounds__(256) void k_mfma(GemmParams a) {
+__global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
   __shared__ MfmaShared<MT> sh;
   __shared__ unsigned long long kbest[MT * 16];
   __shared__ int flag;
@@ -485,7 +500,7 @@ __global__ __launch_bounds__(256) void k_mfma(GemmParams a) {
       const int mt = m >> 4, l = (row >> 2) * 16 + (m & 15), i = row & 3;
       float A = sh.red[0][j][mt][i][l];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) A += sh.red[w][j][mt][i][l];
+      for (int w = 1; w < kStreamWaves; ++w) A += sh.red[w][j][mt][i][l];
       return (A * sh.scale[rr] - sh.cn[rr][m]) + sh.cp[rr][m];
     };
     finish_segment(a, s, rg * kMfmaTileRows, s * kMfmaTileRows, whole, p, value, kbest, &flag);
@@ -530,7 +545,7 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t gr
 
 template <bool Q>
 static hipError_t launch_gemv_m(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
-  const dim3 grid(pl.P), block(256);
+  const dim3 grid(pl.P), block(kThreads);
   switch (p.m) {
 #define W12_GEMV_CASE(MM) \
   case MM: hipLaunchKernelGGL((k_gemv<MM, Q>), grid, block, 0, s, p, p.x); break;
@@ -545,7 +560,7 @@ static hipError_t launch_gemv_m(const GemmPlan& pl, const GemmParams& p, hipStre
 
 template <bool Q>
 static hipError_t launch_mfma_m(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
-  const dim3 grid(pl.P), block(256);
+  const dim3 grid(pl.P), block(kThreads);
   switch ((p.m + 15) / 16) {
     case 1: hipLaunchKernelGGL((k_mfma<1, Q>), grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL((k_mfma<2, Q>), grid, block, 0, s, p); break;

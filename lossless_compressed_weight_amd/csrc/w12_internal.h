@@ -46,11 +46,20 @@ __device__ __forceinline__ uint32_t pk_ashr4(uint32_t p) {
   return __builtin_bit_cast(uint32_t, s);
 }
 
-// v_bfi_b32: (mask & a) | (~mask & b), one instruction.
+// (mask & a) | (~mask & b): the compiler selects v_bfi_b32. Written in C, not
+// inline asm, so the compiler sees a VALU write and keeps the wait states an
+// MFMA reading the result needs.
 __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
-  uint32_t d;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(mask), "v"(a), "v"(b));
-  return d;
+  return (mask & a) | (~mask & b);
+}
+
+// A value held in a VGPR that the compiler may not constant-fold (the empty asm
+// emits no instruction). Keeps 0x38003800 out of folding so that bfi below
+// stays one v_bfi_b32 (SGPR mask, VGPR constant) instead of an AND and an OR
+// with two literals.
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
 }
 
 // Two weights in the GEMM's scaled domain: the exponent field becomes
