@@ -2,27 +2,33 @@
 //
 // SpecPilot (arXiv 2611.02501) section 4.1 and Figure 5b: the kernel decodes
 // records in registers so that the weight stream hides the decode, and splits
-// the reduction loop over workgroups in a fixed order (stream-K), so results
-// are deterministic. Section 4.3: the Q pass reads only the 8-bit view.
+// the reduction over workgroups in a fixed order (stream-K), so results are
+// deterministic. Section 4.3: the Q pass reads only the 8-bit view.
 // Appendix E: the LM head in W12, here fused with a per-row argmax.
 //
-// Work decomposition (both kernels): the matrix is a sequence of row tiles
-// (64 rows for the GEMV kernel, 16 for the MFMA kernel), each a sequence of
-// units of 256 columns along K (one pipeline stage for each of a workgroup's
-// four waves, so trip counts are exact). Workgroup p owns the contiguous unit
-// range [p U / P, (p+1) U / P).
+// Work: the matrix is a sequence of row tiles (64 rows for the GEMV kernel,
+// 16 for the MFMA kernel), each a sequence of units of 256 columns. With P
+// workgroups (one per compute unit) and T tiles, workgroup p owns the whole
+// tiles [p D, (p+1) D), D = T / P, and an even share of the units of the
+// remaining T - P D tiles (stream-K). A segment is the units of one tile (or
+// of a group of whole tiles) that a workgroup processes in one pass.
 //
-// A segment (the units of one tile that a workgroup owns) yields, per output
-// row and activation row, A = sum of x * w' over its columns, where w' is the
-// weight decoded with a fixed exponent bias (w = w' 2^(E_n - 127)), plus the
-// escape corrections of its columns: CN = sum of x * placeholder and CP = sum
-// of x * exact escape value. The segment's value is (A 2^(E_n-127) - CN) + CP.
-// The scales and corrections are gathered by a helper wave while the
-// streaming waves run, so finishing a segment needs no global loads.
+// Each workgroup runs four streaming waves and one helper wave. The streaming
+// waves only stream records and activations: per segment they leave their
+// partial sums in LDS (double-buffered) and raise a counter; they never wait
+// for the helper's memory round trips. The helper does everything with
+// dependent round trips: it adds the partial sums, gathers the per-row scales
+// and escape corrections, and finishes segments - whole tiles by storing
+// them, split tiles by the exchange below. A workgroup streams its (short)
+// split segments first, so their exchange overlaps its whole tiles.
 //
-// A tile covered by one workgroup is finished there. A tile split between
-// workgroups: each stores its segment value in a fixed slot (2p for a
-// workgroup's first tile, 2p+1 for its last) and counts itself in the tile's
+// Segment value, per output row and activation row: A = sum of x * w' over the
+// segment's columns, where w' is the weight decoded with a fixed exponent
+// bias (w = w' 2^(E_n - 127)); CN = sum of x * placeholder and CP = sum of x *
+// exact value over the segment's escapes. The value is (A 2^(E_n-127) - CN) + CP.
+//
+// Split tiles: each workgroup stores its segment value in a fixed slot (2p for
+// its first split tile, 2p+1 for its second) and counts itself in the tile's
 // counter; the last to arrive adds the slots in workgroup order (so the result
 // does not depend on arrival order) and writes the tile. Counters wrap back to
 // zero, so every call leaves them zeroed for the next one.
@@ -31,39 +37,95 @@
 namespace w12 {
 
 constexpr int kUnitCols = 256;
+constexpr int kStreamWaves = 4;
+constexpr int kThreads = (kStreamWaves + 1) * 64;
+constexpr int kSlots = 3;       // segments the helper holds at once
 
-// -------------------------------------------------------------- stream-K map
-__device__ __forceinline__ int64_t unit_start(int64_t p, int64_t units, int P) { return p * units / P; }
-
-// Workgroup owning unit u.
-__device__ __forceinline__ int unit_owner(int64_t u, int64_t units, int P) {
-  return (int)(((u + 1) * P + units - 1) / units) - 1;
+// -------------------------------------------------------------- schedule
+// floor(x / y) for x < 2^40, 0 < y < 2^31: the double quotient is within one
+// of the exact one, and one integer step corrects it. (Inline 64-bit integer
+// division would cost far more code.)
+__device__ __forceinline__ uint32_t div_floor(uint64_t x, uint32_t y) {
+  uint32_t q = (uint32_t)((double)x / (double)y);
+  const uint64_t qy = (uint64_t)q * y;
+  if (qy > x) --q;
+  else if (qy + y <= x) ++q;
+  return q;
 }
 
-__device__ __forceinline__ bool wg_empty(int q, const GemmParams& a) {
-  return unit_start(q, a.units, a.P) == unit_start(q + 1, a.units, a.P);
+// First split unit of workgroup q (q in [0, P]).
+__device__ __forceinline__ uint32_t sk_start(const GemmParams& a, int q) {
+  return (uint32_t)a.sk_base + div_floor((uint64_t)q * (uint64_t)a.sk_units, (uint32_t)a.P);
 }
 
-// Slot of workgroup q's segment of tile t.
-__device__ __forceinline__ int tile_slot(int q, int64_t t, const GemmParams& a) {
-  return (unit_start(q, a.units, a.P) / a.ku == t) ? 2 * q : 2 * q + 1;
+// Workgroup owning split unit u.
+__device__ __forceinline__ int sk_owner(const GemmParams& a, uint32_t u) {
+  const uint64_t v = u - (uint32_t)a.sk_base;
+  return (int)div_floor((v + 1) * (uint64_t)a.P + (uint64_t)a.sk_units - 1, (uint32_t)a.sk_units) - 1;
+}
+
+// Workgroup q's slot for split tile t: 2q if t is its first split tile, 2q+1
+// if its second; -1 if q owns no split unit.
+__device__ __forceinline__ int part_slot(const GemmParams& a, int q, int t) {
+  const uint32_t s = sk_start(a, q), e = sk_start(a, q + 1);
+  if (s == e) return -1;
+  const uint32_t t0 = (uint32_t)t * (uint32_t)a.ku;
+  return 2 * q + ((s >= t0 && s < t0 + (uint32_t)a.ku) ? 0 : 1);
+}
+
+struct Seg {
+  int tile;    // first tile
+  int rg;      // tiles (whole-tile groups of the MFMA kernel; 1 otherwise)
+  int k0, k1;  // units [k0, k1) of each tile
+  int part;    // split tile: 0 or 1 (which of this workgroup's split tiles); -1: whole
+};
+
+// The segments of workgroup p: nsk split ones (shorter first), then whole
+// tiles in groups of at most rmax.
+struct SegList {
+  int n, nsk;
+  Seg sk0, sk1;
+  int dp0, D, rmax;
+};
+
+__device__ __forceinline__ SegList seg_list(const GemmParams& a, int p, int rmax) {
+  SegList L;
+  L.rmax = rmax;
+  L.D = a.dp;
+  L.dp0 = p * a.dp;
+  L.nsk = 0;
+  L.sk0 = L.sk1 = Seg{0, 1, 0, 0, 0};
+  const uint32_t s0 = sk_start(a, p), s1 = sk_start(a, p + 1);
+  if (s1 > s0) {
+    const int ta = (int)div_floor(s0, (uint32_t)a.ku), tb = (int)div_floor(s1 - 1, (uint32_t)a.ku);
+    const uint32_t ua = (uint32_t)ta * (uint32_t)a.ku, ub = (uint32_t)tb * (uint32_t)a.ku;
+    const Seg A{ta, 1, (int)(s0 - ua), ta == tb ? (int)(s1 - ua) : a.ku, 0};
+    if (ta == tb) {
+      L.nsk = 1;
+      L.sk0 = A;
+    } else {
+      const Seg B{tb, 1, 0, (int)(s1 - ub), 1};
+      L.nsk = 2;
+      const bool b_first = (B.k1 - B.k0) < (A.k1 - A.k0);
+      L.sk0 = b_first ? B : A;
+      L.sk1 = b_first ? A : B;
+    }
+  }
+  L.n = L.nsk + (a.dp + rmax - 1) / rmax;
+  return L;
+}
+
+__device__ __forceinline__ Seg seg_at(const GemmParams& a, const SegList& L, int i) {
+  if (i < L.nsk) return i == 0 ? L.sk0 : L.sk1;
+  const int j = i - L.nsk;
+  return Seg{L.dp0 + j * L.rmax, min(L.rmax, L.D - j * L.rmax), 0, a.ku, -1};
 }
 
 // -------------------------------------------------------------- outputs
-__device__ __forceinline__ void emit(const GemmParams& a, int n, int m, float v, unsigned long long* kbest) {
-  if (n >= a.n) return;
-  if (a.mode == kModeStore) {
-    if (a.y_f32) reinterpret_cast<float*>(a.y)[(int64_t)m * a.ldy + n] = v;
-    else reinterpret_cast<uint16_t*>(a.y)[(int64_t)m * a.ldy + n] = f32_to_bf16_rne(v);
-  } else {
-    atomicMax(&kbest[m], argmax_key(v, (uint32_t)n));
-  }
-}
-
-// Cross-workgroup exchange without an L2 writeback: segment values and keys
-// are written and read with agent-scope atomic stores and loads (coherent
-// across the XCDs' separate L2 caches); each thread waits until its own
-// stores are acknowledged, then one thread counts the workgroup in.
+// Cross-workgroup exchange without an L2 writeback: slot values and keys are
+// written and read with agent-scope atomic stores and loads (coherent across
+// the XCDs' separate L2 caches); the helper waits until its stores are
+// acknowledged before it counts the workgroup in.
 __device__ __forceinline__ void store_shared(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -77,88 +139,24 @@ __device__ __forceinline__ unsigned long long load_shared(const unsigned long lo
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Count this workgroup into counter c (n arrivals in all; the counter wraps to
-// 0 on the last). Returns, to every thread, whether this workgroup was last.
-__device__ __forceinline__ bool arrive(uint32_t* c, uint32_t n, int* flag) {
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's coherent stores are acknowledged
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __builtin_amdgcn_atomic_inc32(c, n - 1, __ATOMIC_RELAXED, "agent");
-    *flag = old == n - 1;
-  }
-  __syncthreads();
-  return *flag;
-}
-
-// Finish segment values value(m, row) of tile t (tile_rows rows from output
-// row row0): written directly for a whole tile, through the slots and the
-// tile counter for a split one.
-template <class ValFn>
-__device__ __forceinline__ void finish_segment(const GemmParams& a, int64_t t, int tile_rows, int row0, bool whole,
-                                               int p, ValFn value, unsigned long long* kbest, int* flag) {
-  const int nval = a.m * tile_rows;
-  if (whole) {
-    for (int i = threadIdx.x; i < nval; i += blockDim.x) {
-      const int m = i / tile_rows, row = i % tile_rows;
-      emit(a, row0 + row, m, value(m, row), kbest);
-    }
-    return;
-  }
-  float* dst = a.part + (int64_t)tile_slot(p, t, a) * a.m * tile_rows;
-  for (int i = threadIdx.x; i < nval; i += blockDim.x) {
-    const int m = i / tile_rows, row = i % tile_rows;
-    store_shared(&dst[m * tile_rows + row], value(m, row));
-  }
-  const int64_t u_first = t * a.ku, u_last = min(a.units, (t + 1) * a.ku) - 1;
-  const int pa = unit_owner(u_first, a.units, a.P), pb = unit_owner(u_last, a.units, a.P);
-  uint32_t c = 0;
-  for (int q = pa; q <= pb; ++q) c += !wg_empty(q, a);
-  // a workgroup owns the first unit of at most one split tile, so the owner's
-  // index names the tile's counter
-  if (arrive(&a.ctr[pa], c, flag)) {
-    for (int i = threadIdx.x; i < nval; i += blockDim.x) {
-      const int m = i / tile_rows, row = i % tile_rows;
-      float v = 0.f;
-      for (int q = pa; q <= pb; ++q) {
-        if (wg_empty(q, a)) continue;
-        v += load_shared(&a.part[((int64_t)tile_slot(q, t, a) * a.m + m) * tile_rows + row]);
-      }
-      emit(a, row0 + row, m, v, kbest);
-    }
-  }
-  __syncthreads();
-}
-
-// Argmax mode: publish this workgroup's best key per activation row; the last
-// workgroup to finish reduces all of them into idx / max.
-__device__ __forceinline__ void finish_argmax(const GemmParams& a, int p, unsigned long long* kbest, int* flag) {
-  __syncthreads();
-  if (threadIdx.x < a.m) store_shared(&a.keys[(int64_t)p * a.m + threadIdx.x], kbest[threadIdx.x]);
-  if (arrive(&a.ctr[kMaxGrid], (uint32_t)a.P, flag)) {
-    if (threadIdx.x < a.m) {
-      unsigned long long best = 0ull;
-      for (int q = 0; q < a.P; ++q) {
-        const unsigned long long k = load_shared(&a.keys[(int64_t)q * a.m + threadIdx.x]);
-        best = k > best ? k : best;
-      }
-      a.idx[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
-      if (a.maxv) a.maxv[threadIdx.x] = key_value(best);
-    }
+__device__ __forceinline__ void emit(const GemmParams& a, int n, int m, float v, unsigned long long* kbest) {
+  if (a.mode == kModeStore) {
+    if (a.y_f32) reinterpret_cast<float*>(a.y)[(int64_t)m * a.ldy + n] = v;
+    else reinterpret_cast<uint16_t*>(a.y)[(int64_t)m * a.ldy + n] = f32_to_bf16_rne(v);
+  } else {
+    atomicMax(&kbest[m], argmax_key(v, (uint32_t)n));
   }
 }
 
 // -------------------------------------------------------------- escapes
-// First escape of row n with column >= c0 (binary search in the row's
-// column-sorted list), and the end of the row's list.
-__device__ __forceinline__ uint32_t esc_lower_bound(const GemmParams& a, int n, uint32_t c0, uint32_t* end) {
-  uint32_t lo = a.row_ptr[n], hi = a.row_ptr[n + 1];
-  *end = hi;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (a.esc[mid].x < c0) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
+// The helper gathers a segment's escape corrections in three memory round
+// trips whatever the rows' escape counts (up to a few hundred entries): the
+// row pointers of the segment's rows; all their entries at once (lane = entry),
+// filtered to the segment's columns and appended to a list in LDS; then, with
+// lane = activation row, the activations of 32 or 64 listed entries at a time,
+// summed per row in column order.
+constexpr int kEscLoad = 8;    // entries per lane per load round trip
+constexpr int kEscList = 64 * kEscLoad;
 
 // The weight the main loop used for an escape: its placeholder, seen through
 // the Q view (low nibble 1000) in the Q pass.
@@ -196,23 +194,394 @@ __device__ __forceinline__ void pipeline(int u, int ue, Load&& load, Compute&& c
   if (i < n) compute(sa);
 }
 
+// ============================================================== helper wave
+// Per-segment state the helper keeps in LDS, in slot (segment index % 3):
+// the segment's values [m][row] (first the plain sums A, then the finished
+// values), its corrections CN and CP, and its rows' scales; plus the work
+// list of the corrections.
+template <int MM, int ROWS>
+struct HelperLds {
+  float cv[kSlots][MM][ROWS];
+  float cn[kSlots][MM][ROWS];
+  float cp[kSlots][MM][ROWS];
+  float scale[kSlots][ROWS];
+  unsigned long long kbest[MM];
+  uint32_t rp[3][ROWS + 1];                   // row pointers of each target's rows
+  alignas(16) uint32_t ecol[kEscList];        // listed entries: column,
+  uint32_t ebits[kEscList];                   // original BF16 | placeholder << 16,
+  uint32_t erow[kEscList];                    // target * 256 + row
+  float xs[16][64];          // gathered activations [activation row][entry]
+  float eph[64], eex[64];    // placeholder and exact value of a pass's entries
+  int poff[64];              // exchange: slots of a chunk of participants
+  uint32_t ready[2];  // streaming waves done with the partial buffer (cumulative)
+  uint32_t consumed;  // segments whose partial sums the helper has taken
+};
+
+// Handshakes between the streaming waves and the helper through LDS counters
+// (no barrier, so neither side waits for the other's memory round trips).
+// Every wait ends: the helper waits only for counters the streaming waves
+// raise after each segment, and a streaming wave only for the helper to take
+// the segment two back, which needs nothing from that wave.
+__device__ __forceinline__ void lds_wait_geq(const uint32_t* c, uint32_t v) {
+  while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < v) __builtin_amdgcn_s_sleep(1);
+}
+__device__ __forceinline__ void lds_add(uint32_t* c) {
+  __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_set(uint32_t* c, uint32_t v) {
+  __hip_atomic_store(c, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Upper bound of j in the nondecreasing rp[0 .. rows]: the row holding entry j.
+__device__ __forceinline__ int rp_row(const uint32_t* rp, int rows, uint32_t j) {
+  int lo = 0, hi = rows;  // rp[lo] <= j < rp[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (rp[mid] <= j) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Add the listed entries [0, n) to the corrections, 64 at a time with
+// lane = entry. Entries come sorted by (target, row, column), so each row's
+// entries of a pass are a run of lanes: the activations of all entries are
+// gathered at once (16 activation rows per round trip) and parked in LDS,
+// then the first lane of each run sums the run in column order and adds it
+// to the row's LDS sums (a run split across passes adds its parts in order).
+template <int MM, int ROWS>
+__device__ __forceinline__ void esc_list_apply(const GemmParams& a, HelperLds<MM, ROWS>& h, int n, int slot0,
+                                               int slot1, int slot2, int lane) {
+  // target t's slot is bits 4t .. 4t+3 (arithmetic, not a select, so the
+  // slot stays an index into the LDS arrays)
+  const uint32_t slots = (uint32_t)slot0 | (uint32_t)slot1 << 4 | (uint32_t)slot2 << 8;
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const int ne = min(64, n - e0);
+    const bool live = lane < ne;
+    const int e = e0 + (live ? lane : 0);
+    const uint32_t col = live ? h.ecol[e] : 0u, bits = live ? h.ebits[e] : 0u;
+    const uint32_t tr = live ? h.erow[e] : 0xFFFFFFFFu;
+    const bool head = live && (lane == 0 || h.erow[e - 1] != tr);
+    int len = 0;
+    if (head) {
+      len = 1;
+      while (lane + len < ne && h.erow[e + len] == tr) ++len;
+    }
+    h.eph[lane] = esc_placeholder(a, bits);
+    h.eex[lane] = bf16_to_f32(bits & 0xFFFFu);
+    const uint32_t sl = (slots >> (4 * ((tr >> 8) & 3u))) & 15u, r = tr & 255u;
+    for (int m0 = 0; m0 < a.m; m0 += 16) {
+      float xv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int m = (m0 + j < a.m) ? m0 + j : 0;
+        xv[j] = bf16_to_f32(a.x[(int64_t)m * a.ldx + col]);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) h.xs[j][lane] = xv[j];
+      if (head) {
+        float sn[16], sp[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sn[j] = sp[j] = 0.f;
+        for (int k = 0; k < len; ++k) {
+          const float ph = h.eph[lane + k], ex = h.eex[lane + k];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float x = h.xs[j][lane + k];
+            sn[j] = fmaf(x, ph, sn[j]);
+            sp[j] = fmaf(x, ex, sp[j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (m0 + j < a.m && m0 + j < MM) {
+            h.cn[sl][m0 + j][r] += sn[j];
+            h.cp[sl][m0 + j][r] += sp[j];
+          }
+        }
+      }
+    }
+  }
+}
+
+// A correction target: slot, rows row0 + r for r < rows, columns [c0, c1).
+struct Tgt {
+  int slot, row0, rows;
+  uint32_t c0, c1;
+};
+
+template <class T>
+__device__ __forceinline__ T pick3(int t, T a, T b, T c) { return t == 0 ? a : t == 1 ? b : c; }
+
+// Scales and escape corrections of up to three segments (targets) at once.
+template <int MM, int ROWS>
+__device__ __forceinline__ void corrections(const GemmParams& a, HelperLds<MM, ROWS>& h, int nt, Tgt g0t, Tgt g1t,
+                                            Tgt g2t, int lane) {
+  // row pointers and scales: every load first (clamped indices), one round trip
+  uint32_t etv[3], rpv[3], rpe[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const Tgt T = t == 0 ? g0t : t == 1 ? g1t : g2t;
+    const int n = T.row0 + lane;
+    etv[t] = a.e_top[min(n, a.n - 1)];
+    rpv[t] = a.row_ptr[min(n, a.n)];
+    rpe[t] = a.row_ptr[min(T.row0 + T.rows, a.n)];
+  }
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const Tgt T = t == 0 ? g0t : t == 1 ? g1t : g2t;
+    if (t < nt) {
+      if (lane < T.rows && lane < ROWS) {
+        h.scale[T.slot][lane] = pow2_scale(etv[t]);
+#pragma unroll
+        for (int m = 0; m < MM; ++m) h.cn[T.slot][m][lane] = h.cp[T.slot][m][lane] = 0.f;
+        h.rp[t][lane] = rpv[t];
+      }
+      if (lane == 0) h.rp[t][T.rows] = rpe[t];
+    }
+  }
+  if (!a.fix) return;
+  // the targets' entries as one index space [0, J): target t holds
+  // [pre_t, pre_t + size_t), its entries [E0_t, E0_t + size_t)
+  const uint32_t E00 = __builtin_amdgcn_readfirstlane(h.rp[0][0]);
+  const uint32_t E10 = __builtin_amdgcn_readfirstlane(h.rp[0][g0t.rows]);
+  const uint32_t E01 = nt > 1 ? __builtin_amdgcn_readfirstlane(h.rp[1][0]) : 0u;
+  const uint32_t E11 = nt > 1 ? __builtin_amdgcn_readfirstlane(h.rp[1][g1t.rows]) : 0u;
+  const uint32_t E02 = nt > 2 ? __builtin_amdgcn_readfirstlane(h.rp[2][0]) : 0u;
+  const uint32_t E12 = nt > 2 ? __builtin_amdgcn_readfirstlane(h.rp[2][g2t.rows]) : 0u;
+  const uint32_t pre1 = E10 - E00, pre2 = pre1 + (E11 - E01), J = pre2 + (E12 - E02);
+  for (uint32_t b0 = 0; b0 < J; b0 += kEscList) {
+    uint2 e[kEscLoad];
+    uint32_t gj[kEscLoad];
+    int tt[kEscLoad];
+#pragma unroll
+    for (int k = 0; k < kEscLoad; ++k) {
+      const uint32_t g = b0 + 64 * k + lane;
+      tt[k] = g < pre1 ? 0 : g < pre2 ? 1 : 2;
+      gj[k] = g - pick3(tt[k], 0u, pre1, pre2) + pick3(tt[k], E00, E01, E02);
+      e[k] = g < J ? a.esc[gj[k]] : make_uint2(0xFFFFFFFFu, 0u);
+    }
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < kEscLoad; ++k) {
+      const int t = tt[k];
+      const bool in = b0 + 64 * k + lane < J && e[k].x >= pick3(t, g0t.c0, g1t.c0, g2t.c0) &&
+                      e[k].x < pick3(t, g0t.c1, g1t.c1, g2t.c1);
+      const uint64_t bal = __ballot(in);
+      if (in) {
+        const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        const int r = rp_row(h.rp[t], pick3(t, g0t.rows, g1t.rows, g2t.rows), gj[k]);
+        h.ecol[pos] = e[k].x;
+        h.ebits[pos] = e[k].y;
+        h.erow[pos] = (uint32_t)(t * 256 + r);
+      }
+      n += __popcll(bal);
+    }
+    esc_list_apply(a, h, n, g0t.slot, g1t.slot, g2t.slot, lane);
+  }
+}
+
+// Rows of a segment.
+__device__ __forceinline__ int seg_rows(const Seg& s, int tile_rows) { return s.rg * tile_rows; }
+
+// value = (A * scale - CN) + CP for every (row, m) of slot sl.
+template <int MM, int ROWS>
+__device__ __forceinline__ void apply(const GemmParams& a, HelperLds<MM, ROWS>& h, int sl, int rows, int lane) {
+  if (lane < rows && lane < ROWS) {
+    const float s = h.scale[sl][lane];
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+      if (m < a.m) h.cv[sl][m][lane] = (h.cv[sl][m][lane] * s - h.cn[sl][m][lane]) + h.cp[sl][m][lane];
+  }
+}
+
+// Finish segments s0 .. s0 + count - 1 (held in slots index % 3): whole
+// tiles are written out; split tiles go through the exchange, both at once.
+// In the exchange a lane serves row lane % TR and activation rows
+// lane / TR + (64 / TR) j, so all 64 lanes share a tile's TR x M values.
+template <int MM, int ROWS, int TR>
+__device__ __forceinline__ void finish(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int p,
+                                       int s0, int count, int lane) {
+  constexpr int LPR = 64 / TR;               // lanes per row
+  constexpr int MJ = (MM + LPR - 1) / LPR;   // activation rows per lane
+  constexpr int QC = MJ <= 4 ? 16 : MJ <= 8 ? 8 : 4;  // slots loaded per round trip
+  const int r = lane % TR, mq = lane / TR;
+  int split_seg0 = 0, split_seg1 = 0, nsplit = 0;
+  for (int c = 0; c < count; ++c) {
+    const int si = s0 + c, sl = si % kSlots;
+    const Seg s = seg_at(a, L, si);
+    if (s.part < 0) {
+      const int rows = seg_rows(s, TR), n0 = s.tile * TR;
+      if (lane < rows && lane < ROWS && n0 + lane < a.n) {
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+          if (m < a.m) emit(a, n0 + lane, m, h.cv[sl][m][lane], h.kbest);
+      }
+    } else {
+      // this workgroup's value of the tile, in its fixed slot
+      float* dst = a.part + (int64_t)(2 * p + s.part) * MM * TR;
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) {
+        const int m = mq + LPR * j;
+        if (m < a.m) store_shared(&dst[m * TR + r], h.cv[sl][m][r]);
+      }
+      if (nsplit == 0) split_seg0 = si; else split_seg1 = si;
+      ++nsplit;
+    }
+  }
+  if (nsplit == 0) return;
+  // participants of each split tile and how many own split units (lanes in
+  // parallel, 64 workgroups at a time)
+  int tile_c[2] = {0, 0}, pa_c[2] = {0, 0}, pb_c[2] = {0, 0};
+  uint32_t cnt_c[2] = {0, 0};
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c < nsplit) {
+      const int t = seg_at(a, L, c == 0 ? split_seg0 : split_seg1).tile;
+      const uint32_t u_first = (uint32_t)t * (uint32_t)a.ku;
+      tile_c[c] = t;
+      pa_c[c] = sk_owner(a, u_first);
+      pb_c[c] = sk_owner(a, u_first + (uint32_t)a.ku - 1);
+      for (int q0 = pa_c[c]; q0 <= pb_c[c]; q0 += 64) {
+        const int q = q0 + lane;
+        cnt_c[c] += __popcll(__ballot(q <= pb_c[c] && part_slot(a, q, t) >= 0));
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the slot stores are acknowledged
+  // lane c counts this workgroup into split tile c; a workgroup owns the first
+  // unit of at most one split tile, so the owner's index names the counter
+  bool last = false;
+  if (lane < nsplit) {
+    const uint32_t c = lane == 0 ? cnt_c[0] : cnt_c[1];
+    const int pa = lane == 0 ? pa_c[0] : pa_c[1];
+    last = __builtin_amdgcn_atomic_inc32(&a.ctr[pa], c - 1, __ATOMIC_RELAXED, "agent") == c - 1;
+  }
+  const uint64_t last_mask = __ballot(last);
+  for (int c = 0; c < nsplit; ++c) {
+    if (!((last_mask >> c) & 1)) continue;
+    const int t = c == 0 ? tile_c[0] : tile_c[1];
+    const int pa = c == 0 ? pa_c[0] : pa_c[1], pb = c == 0 ? pb_c[0] : pb_c[1];
+    const int n0 = t * TR;
+    float v[MJ];
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) v[j] = 0.f;
+    bool started = false;  // adds start from the first slot (keeps the sign of a zero sum)
+    for (int q0 = pa; q0 <= pb; q0 += 64) {
+      const int nq = min(64, pb - q0 + 1);
+      h.poff[lane] = lane < nq ? part_slot(a, q0 + lane, t) : -1;
+      for (int i0 = 0; i0 < nq; i0 += QC) {
+        float tv[QC][MJ];
+        int sl[QC];
+#pragma unroll
+        for (int u = 0; u < QC; ++u) {
+          sl[u] = i0 + u < nq ? h.poff[i0 + u] : -1;
+          const int64_t base = (int64_t)max(sl[u], 0) * MM * TR;
+#pragma unroll
+          for (int j = 0; j < MJ; ++j) {
+            const int m = mq + LPR * j;
+            tv[u][j] = (sl[u] >= 0 && m < a.m) ? load_shared(&a.part[base + m * TR + r]) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < QC; ++u) {
+          if (sl[u] < 0) continue;
+#pragma unroll
+          for (int j = 0; j < MJ; ++j) v[j] = started ? v[j] + tv[u][j] : tv[u][j];
+          started = true;
+        }
+      }
+    }
+    if (n0 + r < a.n) {
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) {
+        const int m = mq + LPR * j;
+        if (m < a.m) emit(a, n0 + r, m, v[j], h.kbest);
+      }
+    }
+  }
+}
+
+// Argmax mode: publish this workgroup's best key per activation row; the last
+// workgroup to finish reduces all of them into idx / max.
+template <int MM, int ROWS>
+__device__ __forceinline__ void finish_argmax(const GemmParams& a, HelperLds<MM, ROWS>& h, int p, int lane) {
+  if (lane < a.m) store_shared(&a.keys[(int64_t)p * a.m + lane], h.kbest[lane]);
+  __builtin_amdgcn_s_waitcnt(0);
+  bool last = false;
+  if (lane == 0)
+    last = __builtin_amdgcn_atomic_inc32(&a.ctr[kMaxGrid], (uint32_t)a.P - 1, __ATOMIC_RELAXED, "agent") ==
+           (uint32_t)a.P - 1;
+  if (__ballot(last) == 0) return;
+  if (lane < a.m) {
+    unsigned long long best = 0ull;
+    for (int q = 0; q < a.P; ++q) {
+      const unsigned long long k = load_shared(&a.keys[(int64_t)q * a.m + lane]);
+      best = k > best ? k : best;
+    }
+    a.idx[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+    if (a.maxv) a.maxv[lane] = key_value(best);
+  }
+}
+
+// Correction targets: segments [j0, j1) of the list (at most three).
+template <int MM, int ROWS>
+__device__ __forceinline__ void corrections_for(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L,
+                                                int j0, int j1, int tile_rows, int lane) {
+  const int nt = j1 - j0;
+  if (nt <= 0) return;
+  auto make = [&](int j) {
+    const Seg s = seg_at(a, L, j);
+    return Tgt{j % kSlots, s.tile * tile_rows, seg_rows(s, tile_rows), (uint32_t)s.k0 * kUnitCols,
+               (uint32_t)s.k1 * kUnitCols};
+  };
+  const Tgt z{0, 0, 0, 0, 0};
+  corrections<MM, ROWS>(a, h, nt, make(j0), nt > 1 ? make(j0 + 1) : z, nt > 2 ? make(j0 + 2) : z, lane);
+}
+
+// The helper wave. It first gathers the corrections of the first three
+// segments (at kernel start), then takes each
+// segment's partial sums as the streaming waves leave them: the split
+// segments (streamed first) are finished together through one exchange, the
+// whole-tile segments one by one; corrections of later segments are gathered
+// as their slots free up.
+template <int MM, int ROWS, int TR, class Compact>
+__device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int p,
+                                       int lane, Compact&& compact) {
+  if (lane < MM) h.kbest[lane] = 0ull;
+  const int n = L.n;
+  int corr_end = 0;  // segments [0, corr_end) have their corrections
+  for (int b0 = 0; b0 < n;) {
+    // segments before b0 are finished, so the slots of b0 .. b0 + 2 are free
+    const int ce = min(n, b0 + kSlots);
+    if (corr_end < ce) {
+      corrections_for<MM, ROWS>(a, h, L, corr_end, ce, TR, lane);
+      corr_end = ce;
+    }
+    // the split segments together (one exchange), else one whole-tile segment
+    const int b1 = b0 < L.nsk ? L.nsk : b0 + 1;
+    for (int i = b0; i < b1; ++i) {
+      lds_wait_geq(&h.ready[i & 1], (uint32_t)kStreamWaves * (uint32_t)(i / 2 + 1));
+      compact(i & 1, i % kSlots, seg_at(a, L, i));
+      lds_set(&h.consumed, (uint32_t)(i + 1));
+    }
+    for (int i = b0; i < b1; ++i) apply(a, h, i % kSlots, seg_rows(seg_at(a, L, i), TR), lane);
+    finish<MM, ROWS, TR>(a, h, L, p, b0, b1 - b0, lane);
+    b0 = b1;
+  }
+  if (a.mode == kModeArgmax) finish_argmax(a, h, p, lane);
+}
+
 // ============================================================== GEMV (M < 16)
-// A wave covers 64 rows (lane = row, four 16-row blocks) and one 16-column
-// group per step: each lane loads the 16 view bytes and 8 B-plane bytes of its
-// own row, rebuilds 16 weights and accumulates M dot products. The activations
-// of a step are the same for every lane, so they come through scalar loads and
-// feed v_dot2c_f32_bf16 as its SGPR operand; no cross-lane reduction is
-// needed. In a unit (16 groups) streaming wave w takes groups w, w+4, w+8,
-// w+12; the four waves' sums are added through LDS in wave order.
-//
-// Both kernels run a fifth, helper wave beside the four streaming ones: it
-// reads the per-row scales and gathers the escape corrections of the
-// segment's columns (irregular, latency-bound work with its own wait
-// counters), so the streaming waves never stall on it.
+// A streaming wave covers 64 rows (lane = row, four 16-row blocks) and one
+// 16-column group per step: each lane loads the 16 view bytes and 8 B-plane
+// bytes of its own row, rebuilds 16 weights and accumulates M dot products.
+// The activations of a step are the same for every lane, so they come
+// through scalar loads and feed v_dot2c_f32_bf16 as its SGPR operand; no
+// cross-lane reduction is needed. In a unit (16 groups) streaming wave w
+// takes groups w, w+4, w+8, w+12.
 constexpr int kGemvTileRows = 64;
 constexpr int kGemvSteps = 4;  // column groups per wave per unit
-constexpr int kStreamWaves = 4;
-constexpr int kThreads = (kStreamWaves + 1) * 64;
 
 template <int M, bool Q>
 struct GemvStage {
@@ -222,107 +591,75 @@ struct GemvStage {
 };
 
 template <int M>
-struct GemvShared {
-  float acc[kStreamWaves][M][kGemvTileRows];
-  float cn[M][kGemvTileRows];
-  float cp[M][kGemvTileRows];
-  float scale[kGemvTileRows];
+struct GemvLds {
+  float part[2][kStreamWaves][M][kGemvTileRows];  // streaming waves' sums, double-buffered
+  HelperLds<M, kGemvTileRows> h;
 };
 
 template <int M, bool Q>
 __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t* __restrict__ x) {
-  __shared__ GemvShared<M> sh;
-  __shared__ unsigned long long kbest[M];
-  __shared__ int flag;
+  __shared__ GemvLds<M> sh;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x;
-  const int64_t u0 = unit_start(p, a.units, a.P), u1 = unit_start(p + 1, a.units, a.P);
-  const uint32_t c3800 = opaque_vgpr(0x38003800u);
-  const int64_t ldx = a.ldx;
-  if (threadIdx.x < M) kbest[threadIdx.x] = 0ull;
-  for (int64_t u = u0; u < u1;) {
-    const int tile = (int)(u / a.ku);
-    const int k0 = (int)(u - (int64_t)tile * a.ku);
-    const int k1 = (int)min((int64_t)a.ku, u1 - (int64_t)tile * a.ku);
-    // lane -> row tile*64 + lane; rows past N read block 0 of the tile
-    const int row = tile * kGemvTileRows + lane;
-    const bool ok = row < a.n;
-    if (wave < kStreamWaves) {
-      const uint8_t* tile_rec = a.rec + (int64_t)tile * 4 * a.kb * kRecBytes;
-      const uint32_t soff = ok ? (uint32_t)(lane >> 4) * (uint32_t)(a.kb * kRecBytes) : 0u;
-      const uint32_t voff = soff + (lane & 15) * 16, boff = soff + kViewBytes + (lane & 15) * 8;
-      float acc[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = 0.f;
-      auto load = [&](GemvStage<M, Q>& st, int kk) {
-        st.g = kk * 16 + wave;
-#pragma unroll
-        for (int j = 0; j < kGemvSteps; ++j) {
-          const int gj = st.g + 4 * j;
-          const uint32_t sb = (uint32_t)(gj >> 5) * kRecBytes;
-          st.v[j] = *reinterpret_cast<const uint4*>(tile_rec + (sb + (gj & 31) * 256 + voff));
-          if (!Q) st.b[j] = *reinterpret_cast<const uint2*>(tile_rec + (sb + (gj & 31) * 128 + boff));
-        }
-      };
-      auto compute = [&](const GemvStage<M, Q>& st) {
-#pragma unroll
-        for (int j = 0; j < kGemvSteps; ++j) {
-          const int gj = st.g + 4 * j;
-          uint32_t d[8];
-          decode16_scaled<Q>(st.v[j], Q ? make_uint2(0, 0) : st.b[j], d, c3800);
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const uint32_t* xp = reinterpret_cast<const uint32_t*>(x + (int64_t)m * ldx + gj * 16);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) acc[m] = dot2_bf16(d[t], xp[t], acc[m]);
-          }
-        }
-      };
-      pipeline<GemvStage<M, Q>>(k0, k1, load, compute);
-#pragma unroll
-      for (int m = 0; m < M; ++m) sh.acc[wave][m][lane] = acc[m];
-    } else {
-      // helper: scale and escape corrections of this lane's row over the
-      // segment's columns, in column order
-      float cn[M], cp[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) cn[m] = cp[m] = 0.f;
-      if (a.fix && ok) {
-        uint32_t end;
-        const uint32_t c0 = (uint32_t)k0 * kUnitCols, c1 = (uint32_t)k1 * kUnitCols;
-        for (uint32_t i = esc_lower_bound(a, row, c0, &end); i < end; ++i) {
-          const uint2 e = a.esc[i];
-          if (e.x >= c1) break;
-          const float ph = esc_placeholder(a, e.y), ex = bf16_to_f32(e.y & 0xFFFFu);
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const float xv = bf16_to_f32(x[(int64_t)m * ldx + e.x]);
-            cn[m] = fmaf(xv, ph, cn[m]);
-            cp[m] = fmaf(xv, ex, cp[m]);
-          }
-        }
-      }
+  const SegList L = seg_list(a, p, 1);
+  if (threadIdx.x == 0) sh.h.ready[0] = sh.h.ready[1] = sh.h.consumed = 0;
+  __syncthreads();
+  if (wave == kStreamWaves) {
+    auto compact = [&](int buf, int sl, const Seg&) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        sh.cn[m][lane] = cn[m];
-        sh.cp[m][lane] = cp[m];
-      }
-      sh.scale[lane] = pow2_scale(a.e_top[ok ? row : 0]);
-    }
-    __syncthreads();
-    auto value = [&](int m, int r) {
-      float A = sh.acc[0][m][r];
+        float v = sh.part[buf][0][m][lane];
 #pragma unroll
-      for (int w = 1; w < kStreamWaves; ++w) A += sh.acc[w][m][r];
-      return (A * sh.scale[r] - sh.cn[m][r]) + sh.cp[m][r];
+        for (int w = 1; w < kStreamWaves; ++w) v += sh.part[buf][w][m][lane];
+        sh.h.cv[sl][m][lane] = v;
+      }
     };
-    const bool whole = (k0 == 0 && k1 == a.ku);
-    finish_segment(a, tile, kGemvTileRows, tile * kGemvTileRows, whole, p, value, kbest, &flag);
-    __syncthreads();
-    u = (int64_t)tile * a.ku + k1;
+    helper<M, kGemvTileRows, kGemvTileRows>(a, sh.h, L, p, lane, compact);
+    return;
   }
-  if (a.mode == kModeArgmax) finish_argmax(a, p, kbest, &flag);
+  const uint32_t c3800 = opaque_vgpr(0x38003800u);
+  const int64_t ldx = a.ldx;
+  for (int i = 0; i < L.n; ++i) {
+    const Seg s = seg_at(a, L, i);
+    // lane -> row s.tile * 64 + lane; rows past N read block 0 of the tile
+    const int row = s.tile * kGemvTileRows + lane;
+    const uint8_t* tile_rec = a.rec + (int64_t)s.tile * 4 * a.kb * kRecBytes;
+    const uint32_t soff = row < a.n ? (uint32_t)(lane >> 4) * (uint32_t)(a.kb * kRecBytes) : 0u;
+    const uint32_t voff = soff + (lane & 15) * 16, boff = soff + kViewBytes + (lane & 15) * 8;
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.f;
+    auto load = [&](GemvStage<M, Q>& st, int kk) {
+      st.g = kk * 16 + wave;
+#pragma unroll
+      for (int j = 0; j < kGemvSteps; ++j) {
+        const int gj = st.g + 4 * j;
+        const uint32_t sb = (uint32_t)(gj >> 5) * kRecBytes;
+        st.v[j] = *reinterpret_cast<const uint4*>(tile_rec + (sb + (gj & 31) * 256 + voff));
+        if (!Q) st.b[j] = *reinterpret_cast<const uint2*>(tile_rec + (sb + (gj & 31) * 128 + boff));
+      }
+    };
+    auto compute = [&](const GemvStage<M, Q>& st) {
+#pragma unroll
+      for (int j = 0; j < kGemvSteps; ++j) {
+        const int gj = st.g + 4 * j;
+        uint32_t d[8];
+        decode16_scaled<Q>(st.v[j], Q ? make_uint2(0, 0) : st.b[j], d, c3800);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const uint32_t* xp = reinterpret_cast<const uint32_t*>(x + (int64_t)m * ldx + gj * 16);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[m] = dot2_bf16(d[t], xp[t], acc[m]);
+        }
+      }
+    };
+    pipeline<GemvStage<M, Q>>(s.k0, s.k1, load, compute);
+    if (i >= 2) lds_wait_geq(&sh.h.consumed, (uint32_t)(i - 1));
+#pragma unroll
+    for (int m = 0; m < M; ++m) sh.part[i & 1][wave][m][lane] = acc[m];
+    if (lane == 0) lds_add(&sh.h.ready[i & 1]);
+  }
 }
 
 // ============================================================== MFMA (M >= 16)
@@ -332,14 +669,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t*
 // block gives lane l row l%16 and columns 16 (l/16) .. +15: exactly the A
 // operands of two MFMAs; the B operands use the same lane -> column map.
 // A unit is 4 chunks (256 columns); streaming wave w takes chunk w. Whole
-// 16-row blocks are processed R at a time so one activation load serves R
-// blocks. The four waves' sums are added through LDS in wave order; the
-// helper wave gathers scales and escape corrections meanwhile.
+// 16-row tiles are processed RG at a time so one activation load serves RG
+// tiles.
 constexpr int kMfmaTileRows = 16;
 
-// Blocks per group: 4 up to two m-tiles; 2 beyond, which keeps the kernel's
-// registers within the architectural VGPRs (with four blocks and four m-tiles
-// the compiler's register assignment produced wrong results).
+// Tiles per group: 4 up to two m-tiles, 2 beyond (registers and LDS).
 template <int MT>
 constexpr int kMfmaR = MT <= 2 ? 4 : 2;
 
@@ -351,52 +685,15 @@ struct MfmaStage {
 };
 
 template <int MT>
-struct MfmaShared {
-  float red[kStreamWaves][kMfmaR<MT>][MT][4][64];  // per wave: C of each block and m-tile
-  float cn[kMfmaR<MT> * 16][MT * 16];              // escape corrections per (row, m)
-  float cp[kMfmaR<MT> * 16][MT * 16];
-  float scale[kMfmaR<MT> * 16];
+struct MfmaLds {
+  float part[2][kStreamWaves][kMfmaR<MT>][MT][4][64];  // C of each tile and m-tile, double-buffered
+  HelperLds<MT * 16, kMfmaR<MT> * 16> h;
 };
 
-// One group: RG consecutive 16-row blocks starting at block s, units [k0, k1).
+// One segment: RG consecutive 16-row tiles starting at tile s, units [k0, k1).
 template <int MT, int RG, bool Q>
 __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, int k1, int wave, int lane,
-                                           MfmaShared<MT>& sh) {
-  if (wave == kStreamWaves) {
-    // helper: lane = row of the group; escape corrections for every m, in
-    // column order, sixteen activation rows at a time
-    const int rows = RG * 16;
-    if (lane < rows) {
-      const int n = s * 16 + lane;
-      sh.scale[lane] = pow2_scale(a.e_top[n]);
-      const uint32_t c0 = (uint32_t)k0 * kUnitCols, c1 = (uint32_t)k1 * kUnitCols;
-      uint32_t end = 0, first = 0;
-      if (a.fix) first = esc_lower_bound(a, n, c0, &end);
-      for (int m0 = 0; m0 < a.m; m0 += 16) {
-        float cn[16], cp[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) cn[j] = cp[j] = 0.f;
-        for (uint32_t i = first; i < end; ++i) {
-          const uint2 e = a.esc[i];
-          if (e.x >= c1) break;
-          const float ph = esc_placeholder(a, e.y), ex = bf16_to_f32(e.y & 0xFFFFu);
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int m = min(m0 + j, a.m - 1);
-            const float xv = bf16_to_f32(a.x[(int64_t)m * a.ldx + e.x]);
-            cn[j] = fmaf(xv, ph, cn[j]);
-            cp[j] = fmaf(xv, ex, cp[j]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          sh.cn[lane][m0 + j] = cn[j];
-          sh.cp[lane][m0 + j] = cp[j];
-        }
-      }
-    }
-    return;
-  }
+                                           float (*part)[kMfmaR<MT>][MT][4][64], int seg, const uint32_t* consumed) {
   f32x4_t acc[RG][MT];
 #pragma unroll
   for (int j = 0; j < RG; ++j)
@@ -451,91 +748,87 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
     }
   };
   pipeline<MfmaStage<MT, RG, Q>>(k0, k1, load, compute);
+  if (seg >= 2) lds_wait_geq(consumed, (uint32_t)(seg - 1));
   // C layout of a 16x16 MFMA: lane l holds rows 4 (l/16) + i, column l % 16.
 #pragma unroll
   for (int j = 0; j < RG; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sh.red[wave][j][mt][i][lane] = acc[j][mt][i];
+      for (int i = 0; i < 4; ++i) part[wave][j][mt][i][lane] = acc[j][mt][i];
 }
 
 template <int MT, bool Q>
 __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
-  __shared__ MfmaShared<MT> sh;
-  __shared__ unsigned long long kbest[MT * 16];
-  __shared__ int flag;
+  __shared__ MfmaLds<MT> sh;
+  constexpr int R = kMfmaR<MT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x;
-  const int64_t u0 = unit_start(p, a.units, a.P), u1 = unit_start(p + 1, a.units, a.P);
-  if (threadIdx.x < MT * 16) kbest[threadIdx.x] = 0ull;
-  for (int64_t u = u0; u < u1;) {
-    const int s = (int)(u / a.ku);
-    const int k0 = (int)(u - (int64_t)s * a.ku);
-    int rg, k1;
-    if (k0 == 0 && (int64_t)(s + 1) * a.ku <= u1) {
-      rg = (int)min((int64_t)kMfmaR<MT>, (u1 - u) / a.ku);
-      k1 = a.ku;
-    } else {
-      rg = 1;
-      k1 = (int)min((int64_t)a.ku, u1 - (int64_t)s * a.ku);
-    }
-    if constexpr (kMfmaR<MT> == 4) {
-      switch (rg) {
-        case 1: mfma_group<MT, 1, Q>(a, s, k0, k1, wave, lane, sh); break;
-        case 2: mfma_group<MT, 2, Q>(a, s, k0, k1, wave, lane, sh); break;
-        case 3: mfma_group<MT, 3, Q>(a, s, k0, k1, wave, lane, sh); break;
-        default: mfma_group<MT, 4, Q>(a, s, k0, k1, wave, lane, sh); break;
+  const SegList L = seg_list(a, p, R);
+  if (threadIdx.x == 0) sh.h.ready[0] = sh.h.ready[1] = sh.h.consumed = 0;
+  __syncthreads();
+  if (wave == kStreamWaves) {
+    // C of tile j at (row, m): lane (row/4)*16 + m%16, element row%4, m-tile m/16
+    auto compact = [&](int buf, int sl, const Seg& s) {
+      const int rr = lane;
+      if (rr < s.rg * 16) {
+        const int j = rr >> 4, row = rr & 15, i = row & 3, lb = (row >> 2) * 16;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int mm = 0; mm < 16; ++mm) {
+            float v = sh.part[buf][0][j][mt][i][lb + mm];
+#pragma unroll
+            for (int w = 1; w < kStreamWaves; ++w) v += sh.part[buf][w][j][mt][i][lb + mm];
+            sh.h.cv[sl][mt * 16 + mm][rr] = v;
+          }
+      }
+    };
+    helper<MT * 16, R * 16, kMfmaTileRows>(a, sh.h, L, p, lane, compact);
+    return;
+  }
+  for (int i = 0; i < L.n; ++i) {
+    const Seg s = seg_at(a, L, i);
+    if constexpr (R == 4) {
+      switch (s.rg) {
+        case 1: mfma_group<MT, 1, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
+        case 2: mfma_group<MT, 2, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
+        case 3: mfma_group<MT, 3, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
+        default: mfma_group<MT, 4, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
       }
     } else {
-      if (rg == 1) mfma_group<MT, 1, Q>(a, s, k0, k1, wave, lane, sh);
-      else mfma_group<MT, 2, Q>(a, s, k0, k1, wave, lane, sh);
+      if (s.rg == 1) mfma_group<MT, 1, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed);
+      else mfma_group<MT, 2, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed);
     }
-    __syncthreads();
-    const bool whole = (k0 == 0 && k1 == a.ku);
-    // C of block j at (row, m): lane (row/4)*16 + m%16, element row%4, m-tile m/16
-    auto value = [&](int m, int rr) {
-      const int j = rr >> 4, row = rr & 15;
-      const int mt = m >> 4, l = (row >> 2) * 16 + (m & 15), i = row & 3;
-      float A = sh.red[0][j][mt][i][l];
-#pragma unroll
-      for (int w = 1; w < kStreamWaves; ++w) A += sh.red[w][j][mt][i][l];
-      return (A * sh.scale[rr] - sh.cn[rr][m]) + sh.cp[rr][m];
-    };
-    finish_segment(a, s, rg * kMfmaTileRows, s * kMfmaTileRows, whole, p, value, kbest, &flag);
-    __syncthreads();
-    u = (int64_t)(s + rg - 1) * a.ku + k1;
+    if (lane == 0) lds_add(&sh.h.ready[i & 1]);
   }
-  if (a.mode == kModeArgmax) finish_argmax(a, p, kbest, &flag);
 }
 
 // ============================================================== planning
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t grid_override) {
   GemmPlan pl{};
   pl.mfma = (path == 2) || (path == 0 && m >= 16);
+  pl.ku = (int)(k / kUnitCols);
   if (pl.mfma) {
     pl.tile_rows = kMfmaTileRows;
-    pl.ku = (int)(k / kUnitCols);
-    pl.tiles = (int)(n / 16);
+    pl.tiles = (int)(n / kMfmaTileRows);
   } else {
     pl.tile_rows = kGemvTileRows;
-    pl.ku = (int)(k / kUnitCols);
     pl.tiles = (int)((n + kGemvTileRows - 1) / kGemvTileRows);
   }
   pl.units = (int64_t)pl.tiles * pl.ku;
-  // One resident round of workgroups (occupancy set by the kernels' register
-  // and LDS use); at least a few units per workgroup.
-  const int64_t mt = (m + 15) / 16;
-  const int64_t per_cu = pl.mfma ? (mt == 1 ? 4 : 2) : 4;
-  int64_t P = kNumCU * per_cu;
-  const int64_t min_units = 2;
-  if (pl.units / min_units < P) P = pl.units / min_units;
+  // One workgroup per compute unit: its four streaming waves keep enough
+  // loads in flight, and the whole tiles go round-robin over the CUs.
+  int64_t P = kNumCU;
   if (grid_override > 0) P = grid_override;
   if (P > kMaxGrid) P = kMaxGrid;
   if (P > pl.units) P = pl.units;
   if (P < 1) P = 1;
   pl.P = (int)P;
+  pl.dp = (int)(pl.tiles / P);
+  pl.sk_base = (int64_t)P * pl.dp * pl.ku;
+  pl.sk_units = pl.units - pl.sk_base;
   const int64_t mm = pl.mfma ? ((m + 15) / 16) * 16 : m;
   pl.ctr_bytes = kCounterBytes;
   pl.part_bytes = (size_t)(2 * P) * (size_t)mm * pl.tile_rows * sizeof(float);
@@ -577,6 +870,9 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmParams p, hipStream_t s, int* uns
   p.ku = pl.ku;
   p.tiles = pl.tiles;
   p.P = pl.P;
+  p.dp = pl.dp;
+  p.sk_base = pl.sk_base;
+  p.sk_units = pl.sk_units;
   if (!pl.mfma && p.m > 16) {
     *unsupported = 1;
     return hipSuccess;

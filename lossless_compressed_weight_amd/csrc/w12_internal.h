@@ -142,12 +142,15 @@ struct GemmParams {
   unsigned long long* keys;  // per-workgroup argmax keys [P][M]
   int32_t* idx;              // argmax outputs [M]
   float* maxv;               // argmax values [M] (may be null)
-  int64_t units;             // stream-K work units in the whole matrix
+  int64_t units;             // work units (tile x 256 columns) in the whole matrix
+  int64_t sk_base;           // first unit of the split (stream-K) tiles
+  int64_t sk_units;          // units of the split tiles
   int n, k;
   int kb;                    // records per 16-row block (K / 512)
   int ku;                    // units per tile
   int tiles;
   int P;                     // workgroups
+  int dp;                    // whole tiles per workgroup
   int m;                     // activation rows
   int y_f32;
   int mode;                  // 0 = store Y, 1 = argmax keys
@@ -171,7 +174,9 @@ struct GemmPlan {
   int tile_rows;
   int ku;
   int tiles;
+  int dp;
   int64_t units;
+  int64_t sk_base, sk_units;
   size_t ctr_bytes;
   size_t part_bytes;
   size_t key_bytes;
