@@ -55,9 +55,10 @@ int check_gemm_args(const w12_matrix* m, const void* x, int64_t M, int64_t ldx, 
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// workspace: [counters | partial slots | argmax keys], each 256-byte aligned
+// workspace: [counters | partial slots | argmax keys | transposed x], each
+// 256-byte aligned
 size_t gemm_ws_bytes(const GemmPlan& pl) {
-  return round256(pl.ctr_bytes) + round256(pl.part_bytes) + round256(pl.key_bytes);
+  return round256(pl.ctr_bytes) + round256(pl.part_bytes) + round256(pl.key_bytes) + round256(pl.xt_bytes);
 }
 
 GemmPlan make_plan(int64_t n, int64_t k, int64_t M, int op) {
@@ -94,8 +95,20 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   p.mode = op == W12_OP_LMHEAD_ARGMAX ? kModeArgmax : kModeStore;
   p.fix = fix && m->n_esc > 0;
   p.q = op == W12_OP_GEMM_Q8;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // The MFMA kernel's escape fix-up reads the activations of an escape column
+  // for all rows at once from a transposed copy of x (one cache line instead
+  // of one per activation row).
+  p.xt = nullptr;
+  if (pl.mfma && p.fix && pl.xt_bytes > 0) {
+    uint16_t* xt = reinterpret_cast<uint16_t*>(wsb + round256(pl.ctr_bytes) + round256(pl.part_bytes) +
+                                               round256(pl.key_bytes));
+    const hipError_t ex = launch_xpose(x, ldx, (int)M, (int)(((M + 15) / 16) * 16), (int)m->k, xt, st);
+    if (ex != hipSuccess) return hip_fail(ex, "activation transpose launch");
+    p.xt = xt;
+  }
   int unsupported = 0;
-  const hipError_t e = launch_gemm(pl, p, reinterpret_cast<hipStream_t>(stream), &unsupported);
+  const hipError_t e = launch_gemm(pl, p, st, &unsupported);
   if (unsupported) return W12_E_M_RANGE;
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return W12_OK;

@@ -248,7 +248,7 @@ __device__ __forceinline__ int rp_row(const uint32_t* rp, int rows, uint32_t j) 
 // gathered at once (16 activation rows per round trip) and parked in LDS,
 // then the first lane of each run sums the run in column order and adds it
 // to the row's LDS sums (a run split across passes adds its parts in order).
-template <int MM, int ROWS>
+template <int MM, int ROWS, bool XT>
 __device__ __forceinline__ void esc_list_apply(const GemmParams& a, HelperLds<MM, ROWS>& h, int n, int slot0,
                                                int slot1, int slot2, int lane) {
   // target t's slot is bits 4t .. 4t+3 (arithmetic, not a select, so the
@@ -269,15 +269,37 @@ __device__ __forceinline__ void esc_list_apply(const GemmParams& a, HelperLds<MM
     h.eph[lane] = esc_placeholder(a, bits);
     h.eex[lane] = bf16_to_f32(bits & 0xFFFFu);
     const uint32_t sl = (slots >> (4 * ((tr >> 8) & 3u))) & 15u, r = tr & 255u;
-    for (int m0 = 0; m0 < a.m; m0 += 16) {
-      float xv[16];
+    // XT: the entry's activations for all rows, one line of the transposed copy
+    constexpr int XW = XT ? MM / 2 : 1;
+    uint32_t xw[XW];
+    if constexpr (XT) {
+      const uint4* xp = reinterpret_cast<const uint4*>(a.xt + (size_t)col * MM);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = (m0 + j < a.m) ? m0 + j : 0;
-        xv[j] = bf16_to_f32(a.x[(int64_t)m * a.ldx + col]);
+      for (int i = 0; i < MM / 8; ++i) {
+        const uint4 v = xp[i];
+        xw[4 * i] = v.x, xw[4 * i + 1] = v.y, xw[4 * i + 2] = v.z, xw[4 * i + 3] = v.w;
       }
+    }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) h.xs[j][lane] = xv[j];
+    for (int m0 = 0; m0 < (XT ? MM : 64); m0 += 16) {
+      if (m0 >= a.m) break;
+      if constexpr (XT) {
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          const uint32_t w = xw[(m0 + j) / 2];
+          h.xs[j][lane] = bf16_to_f32(w & 0xFFFFu);
+          h.xs[j + 1][lane] = bf16_to_f32(w >> 16);
+        }
+      } else {
+        float xv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int m = (m0 + j < a.m) ? m0 + j : 0;
+          xv[j] = bf16_to_f32(a.x[(int64_t)m * a.ldx + col]);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) h.xs[j][lane] = xv[j];
+      }
       if (head) {
         float sn[16], sp[16];
 #pragma unroll
@@ -313,7 +335,7 @@ template <class T>
 __device__ __forceinline__ T pick3(int t, T a, T b, T c) { return t == 0 ? a : t == 1 ? b : c; }
 
 // Scales and escape corrections of up to three segments (targets) at once.
-template <int MM, int ROWS>
+template <int MM, int ROWS, bool XT>
 __device__ __forceinline__ void corrections(const GemmParams& a, HelperLds<MM, ROWS>& h, int nt, Tgt g0t, Tgt g1t,
                                             Tgt g2t, int lane) {
   // row pointers and scales: every load first (clamped indices), one round trip
@@ -377,7 +399,7 @@ __device__ __forceinline__ void corrections(const GemmParams& a, HelperLds<MM, R
       }
       n += __popcll(bal);
     }
-    esc_list_apply(a, h, n, g0t.slot, g1t.slot, g2t.slot, lane);
+    esc_list_apply<MM, ROWS, XT>(a, h, n, g0t.slot, g1t.slot, g2t.slot, lane);
   }
 }
 
@@ -525,7 +547,7 @@ __device__ __forceinline__ void finish_argmax(const GemmParams& a, HelperLds<MM,
 }
 
 // Correction targets: segments [j0, j1) of the list (at most three).
-template <int MM, int ROWS>
+template <int MM, int ROWS, bool XT>
 __device__ __forceinline__ void corrections_for(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L,
                                                 int j0, int j1, int tile_rows, int lane) {
   const int nt = j1 - j0;
@@ -536,7 +558,7 @@ __device__ __forceinline__ void corrections_for(const GemmParams& a, HelperLds<M
                (uint32_t)s.k1 * kUnitCols};
   };
   const Tgt z{0, 0, 0, 0, 0};
-  corrections<MM, ROWS>(a, h, nt, make(j0), nt > 1 ? make(j0 + 1) : z, nt > 2 ? make(j0 + 2) : z, lane);
+  corrections<MM, ROWS, XT>(a, h, nt, make(j0), nt > 1 ? make(j0 + 1) : z, nt > 2 ? make(j0 + 2) : z, lane);
 }
 
 // The helper wave. It first gathers the corrections of the first three
@@ -555,7 +577,7 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
     // segments before b0 are finished, so the slots of b0 .. b0 + 2 are free
     const int ce = min(n, b0 + kSlots);
     if (corr_end < ce) {
-      corrections_for<MM, ROWS>(a, h, L, corr_end, ce, TR, lane);
+      corrections_for<MM, ROWS, TR == 16>(a, h, L, corr_end, ce, TR, lane);
       corr_end = ce;
     }
     // the split segments together (one exchange), else one whole-tile segment
@@ -805,6 +827,30 @@ __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
   }
 }
 
+// ============================================================== activation transpose
+// x [M, K] -> xt [K, MM]: 64 columns per workgroup through LDS, both sides
+// read and written in rows.
+__global__ __launch_bounds__(256) void k_xpose(const uint16_t* __restrict__ x, int64_t ldx, int M, int MM,
+                                               uint16_t* __restrict__ xt) {
+  __shared__ uint16_t t[64][65];
+  const int c0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < MM * 64; i += 256) {
+    const int m = i >> 6, c = i & 63;
+    t[m][c] = m < M ? x[(int64_t)m * ldx + c0 + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * MM; i += 256) {
+    const int c = i / MM, m = i - c * MM;
+    xt[(int64_t)(c0 + c) * MM + m] = t[m][c];
+  }
+}
+
+hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, uint16_t* xt, hipStream_t s) {
+  if (mm > 64 || M > mm || K % 64 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_xpose, dim3(K / 64), dim3(256), 0, s, x, ldx, M, mm, xt);
+  return hipGetLastError();
+}
+
 // ============================================================== planning
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t grid_override) {
   GemmPlan pl{};
@@ -833,6 +879,7 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t gr
   pl.ctr_bytes = kCounterBytes;
   pl.part_bytes = (size_t)(2 * P) * (size_t)mm * pl.tile_rows * sizeof(float);
   pl.key_bytes = (op == W12_OP_LMHEAD_ARGMAX) ? (size_t)P * (size_t)m * 8 : 0;
+  pl.xt_bytes = pl.mfma ? (size_t)k * (size_t)mm * sizeof(uint16_t) : 0;
   return pl;
 }
 

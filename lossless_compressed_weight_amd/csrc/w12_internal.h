@@ -135,6 +135,7 @@ struct GemmParams {
   const uint2* esc;          // w12_escape as {col, bits | ph << 16}
   const uint16_t* x;
   int64_t ldx;
+  const uint16_t* xt;        // x transposed, [K][16 * ceil(M / 16)], rows past M zero (or null)
   void* y;
   int64_t ldy;
   uint32_t* ctr;             // split-tile counters [tiles], then the argmax counter; zero between calls
@@ -180,8 +181,11 @@ struct GemmPlan {
   size_t ctr_bytes;
   size_t part_bytes;
   size_t key_bytes;
+  size_t xt_bytes;
 };
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t grid_override);
 hipError_t launch_gemm(const GemmPlan& plan, GemmParams p, hipStream_t s, int* unsupported);
+// x [M, K] (row stride ldx) -> xt [K, mm] (mm = 16 * ceil(M / 16)), rows past M zero.
+hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, uint16_t* xt, hipStream_t s);
 
 }  // namespace w12
