@@ -27,11 +27,12 @@
 // bias (w = w' 2^(E_n - 127)); CN = sum of x * placeholder and CP = sum of x *
 // exact value over the segment's escapes. The value is (A 2^(E_n-127) - CN) + CP.
 //
-// Split tiles: each workgroup stores its segment value in a fixed slot (2p for
-// its first split tile, 2p+1 for its second) and counts itself in the tile's
-// counter; the last to arrive adds the slots in workgroup order (so the result
-// does not depend on arrival order) and writes the tile. Counters wrap back to
-// zero, so every call leaves them zeroed for the next one.
+// Split tiles: each workgroup stores its scaled sum A 2^(E_n-127) in a fixed
+// slot (2p for its first split tile, 2p+1 for its second) and counts itself
+// in the tile's counter; the last to arrive adds the slots in workgroup order
+// (so the result does not depend on arrival order), applies the tile's escape
+// corrections over all its columns - (sum - CN) + CP - and writes the tile.
+// Counters wrap back to zero, so every call leaves them zeroed for the next one.
 #include "w12_internal.h"
 
 namespace w12 {
@@ -210,7 +211,7 @@ struct HelperLds {
   alignas(16) uint32_t ecol[kEscList];        // listed entries: column,
   uint32_t ebits[kEscList];                   // original BF16 | placeholder << 16,
   uint32_t erow[kEscList];                    // target * 256 + row
-  float xs[16][64];          // gathered activations [activation row][entry]
+  alignas(16) float xs[64][20];  // gathered activations [entry][activation row], rows padded
   float eph[64], eex[64];    // placeholder and exact value of a pass's entries
   int poff[64];              // exchange: slots of a chunk of participants
   uint32_t ready[2];  // streaming waves done with the partial buffer (cumulative)
@@ -283,41 +284,57 @@ __device__ __forceinline__ void esc_list_apply(const GemmParams& a, HelperLds<MM
 #pragma unroll
     for (int m0 = 0; m0 < (XT ? MM : 64); m0 += 16) {
       if (m0 >= a.m) break;
+      float xv[16];
       if constexpr (XT) {
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
           const uint32_t w = xw[(m0 + j) / 2];
-          h.xs[j][lane] = bf16_to_f32(w & 0xFFFFu);
-          h.xs[j + 1][lane] = bf16_to_f32(w >> 16);
+          xv[j] = bf16_to_f32(w & 0xFFFFu);
+          xv[j + 1] = bf16_to_f32(w >> 16);
         }
       } else {
-        float xv[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int m = (m0 + j < a.m) ? m0 + j : 0;
           xv[j] = bf16_to_f32(a.x[(int64_t)m * a.ldx + col]);
         }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) h.xs[j][lane] = xv[j];
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(&h.xs[lane][4 * q]) =
+            make_float4(xv[4 * q], xv[4 * q + 1], xv[4 * q + 2], xv[4 * q + 3]);
       if (head) {
         float sn[16], sp[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) sn[j] = sp[j] = 0.f;
         for (int k = 0; k < len; ++k) {
           const float ph = h.eph[lane + k], ex = h.eex[lane + k];
+          float xk[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(&h.xs[lane + k][4 * q]);
+            xk[4 * q] = v.x, xk[4 * q + 1] = v.y, xk[4 * q + 2] = v.z, xk[4 * q + 3] = v.w;
+          }
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const float x = h.xs[j][lane + k];
-            sn[j] = fmaf(x, ph, sn[j]);
-            sp[j] = fmaf(x, ex, sp[j]);
+            sn[j] = fmaf(xk[j], ph, sn[j]);
+            sp[j] = fmaf(xk[j], ex, sp[j]);
           }
+        }
+        // all reads before any write (the compiler cannot tell the LDS
+        // addresses apart and would otherwise wait on each access)
+        float on[16], op[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int m = m0 + j < MM ? m0 + j : MM - 1;
+          on[j] = h.cn[sl][m][r];
+          op[j] = h.cp[sl][m][r];
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           if (m0 + j < a.m && m0 + j < MM) {
-            h.cn[sl][m0 + j][r] += sn[j];
-            h.cp[sl][m0 + j][r] += sp[j];
+            h.cn[sl][m0 + j][r] = on[j] + sn[j];
+            h.cp[sl][m0 + j][r] = op[j] + sp[j];
           }
         }
       }
@@ -334,10 +351,12 @@ struct Tgt {
 template <class T>
 __device__ __forceinline__ T pick3(int t, T a, T b, T c) { return t == 0 ? a : t == 1 ? b : c; }
 
-// Scales and escape corrections of up to three segments (targets) at once.
-template <int MM, int ROWS, bool XT>
-__device__ __forceinline__ void corrections(const GemmParams& a, HelperLds<MM, ROWS>& h, int nt, Tgt g0t, Tgt g1t,
-                                            Tgt g2t, int lane) {
+// Scales and escape corrections of up to three segments (targets) at once,
+// in two steps: corr_rows (row pointers and scales; sums cleared), then
+// corr_list (entries, activations, sums).
+template <int MM, int ROWS>
+__device__ __forceinline__ void corr_rows(const GemmParams& a, HelperLds<MM, ROWS>& h, int nt, Tgt g0t, Tgt g1t,
+                                          Tgt g2t, int lane) {
   // row pointers and scales: every load first (clamped indices), one round trip
   uint32_t etv[3], rpv[3], rpe[3];
 #pragma unroll
@@ -361,6 +380,11 @@ __device__ __forceinline__ void corrections(const GemmParams& a, HelperLds<MM, R
       if (lane == 0) h.rp[t][T.rows] = rpe[t];
     }
   }
+}
+
+template <int MM, int ROWS, bool XT>
+__device__ __forceinline__ void corr_list(const GemmParams& a, HelperLds<MM, ROWS>& h, int nt, Tgt g0t, Tgt g1t,
+                                          Tgt g2t, int lane) {
   if (!a.fix) return;
   // the targets' entries as one index space [0, J): target t holds
   // [pre_t, pre_t + size_t), its entries [E0_t, E0_t + size_t)
@@ -403,87 +427,136 @@ __device__ __forceinline__ void corrections(const GemmParams& a, HelperLds<MM, R
   }
 }
 
+template <int MM, int ROWS, bool XT>
+__device__ __forceinline__ void corrections(const GemmParams& a, HelperLds<MM, ROWS>& h, int nt, Tgt g0t, Tgt g1t,
+                                            Tgt g2t, int lane) {
+  corr_rows(a, h, nt, g0t, g1t, g2t, lane);
+  corr_list<MM, ROWS, XT>(a, h, nt, g0t, g1t, g2t, lane);
+}
+
 // Rows of a segment.
 __device__ __forceinline__ int seg_rows(const Seg& s, int tile_rows) { return s.rg * tile_rows; }
 
 // value = (A * scale - CN) + CP for every (row, m) of slot sl.
+// (Each chunk of 8 is read before it is written: the compiler cannot tell
+// the LDS addresses apart and would otherwise wait on every access.)
 template <int MM, int ROWS>
 __device__ __forceinline__ void apply(const GemmParams& a, HelperLds<MM, ROWS>& h, int sl, int rows, int lane) {
   if (lane < rows && lane < ROWS) {
     const float s = h.scale[sl][lane];
 #pragma unroll
-    for (int m = 0; m < MM; ++m)
-      if (m < a.m) h.cv[sl][m][lane] = (h.cv[sl][m][lane] * s - h.cn[sl][m][lane]) + h.cp[sl][m][lane];
+    for (int m0 = 0; m0 < MM; m0 += 8) {
+      float c[8], cn[8], cp[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int m = m0 + j < MM ? m0 + j : MM - 1;
+        c[j] = h.cv[sl][m][lane], cn[j] = h.cn[sl][m][lane], cp[j] = h.cp[sl][m][lane];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (m0 + j < MM && m0 + j < a.m) h.cv[sl][m0 + j][lane] = (c[j] * s - cn[j]) + cp[j];
+    }
   }
 }
 
-// Finish segments s0 .. s0 + count - 1 (held in slots index % 3): whole
-// tiles are written out; split tiles go through the exchange, both at once.
-// In the exchange a lane serves row lane % TR and activation rows
-// lane / TR + (64 / TR) j, so all 64 lanes share a tile's TR x M values.
-template <int MM, int ROWS, int TR>
-__device__ __forceinline__ void finish(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int p,
-                                       int s0, int count, int lane) {
-  constexpr int LPR = 64 / TR;               // lanes per row
-  constexpr int MJ = (MM + LPR - 1) / LPR;   // activation rows per lane
-  constexpr int QC = MJ <= 4 ? 16 : MJ <= 8 ? 8 : 4;  // slots loaded per round trip
-  const int r = lane % TR, mq = lane / TR;
-  int split_seg0 = 0, split_seg1 = 0, nsplit = 0;
-  for (int c = 0; c < count; ++c) {
-    const int si = s0 + c, sl = si % kSlots;
-    const Seg s = seg_at(a, L, si);
-    if (s.part < 0) {
-      const int rows = seg_rows(s, TR), n0 = s.tile * TR;
-      if (lane < rows && lane < ROWS && n0 + lane < a.n) {
+// value = A * scale for every (row, m) of slot sl (a split segment: its
+// corrections are applied once, to the tile's sum).
+template <int MM, int ROWS>
+__device__ __forceinline__ void scale_only(const GemmParams& a, HelperLds<MM, ROWS>& h, int sl, int rows, int lane) {
+  if (lane < rows && lane < ROWS) {
+    const float s = h.scale[sl][lane];
 #pragma unroll
-        for (int m = 0; m < MM; ++m)
-          if (m < a.m) emit(a, n0 + lane, m, h.cv[sl][m][lane], h.kbest);
-      }
-    } else {
-      // this workgroup's value of the tile, in its fixed slot
+    for (int m0 = 0; m0 < MM; m0 += 8) {
+      float c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = h.cv[sl][m0 + j < MM ? m0 + j : MM - 1][lane];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (m0 + j < MM && m0 + j < a.m) h.cv[sl][m0 + j][lane] = c[j] * s;
+    }
+  }
+}
+
+// Whole-tile segment si (slot si % 3): its finished values are written out.
+template <int MM, int ROWS, int TR>
+__device__ __forceinline__ void emit_whole(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int si,
+                                           int lane) {
+  const Seg s = seg_at(a, L, si);
+  const int sl = si % kSlots, rows = seg_rows(s, TR), n0 = s.tile * TR;
+  if (lane < rows && lane < ROWS && n0 + lane < a.n) {
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+      if (m < a.m) emit(a, n0 + lane, m, h.cv[sl][m][lane], h.kbest);
+  }
+}
+
+// The exchange of a workgroup's split segments (0 .. nsk-1, slots 0 and 1).
+// Begin: store this workgroup's scaled sums A 2^(E_n-127) in its fixed slots,
+// then count it into each tile. End: for the tiles it was last on, add all
+// slots in workgroup order and apply the tile's escape corrections over all
+// its columns: value = (sum - CN) + CP. In the exchange a lane serves row
+// lane % TR and activation rows lane / TR + (64 / TR) j.
+struct Xch {
+  int n;              // split segments
+  int t0, t1;         // their tiles
+  int pa0, pa1, pb0, pb1;  // participants of each tile
+  uint64_t last;      // bit c: this workgroup finishes tile c
+};
+
+template <int MM, int ROWS, int TR>
+__device__ __forceinline__ Xch xch_begin(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int p,
+                                         int lane) {
+  constexpr int LPR = 64 / TR;
+  constexpr int MJ = (MM + LPR - 1) / LPR;
+  const int r = lane % TR, mq = lane / TR;
+  Xch X{L.nsk, 0, 0, 0, 0, 0, 0, 0ull};
+  uint32_t cnt0 = 0, cnt1 = 0;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c < X.n) {
+      const Seg s = seg_at(a, L, c);
       float* dst = a.part + (int64_t)(2 * p + s.part) * MM * TR;
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
         const int m = mq + LPR * j;
-        if (m < a.m) store_shared(&dst[m * TR + r], h.cv[sl][m][r]);
+        if (m < a.m) store_shared(&dst[m * TR + r], h.cv[c][m][r]);
       }
-      if (nsplit == 0) split_seg0 = si; else split_seg1 = si;
-      ++nsplit;
-    }
-  }
-  if (nsplit == 0) return;
-  // participants of each split tile and how many own split units (lanes in
-  // parallel, 64 workgroups at a time)
-  int tile_c[2] = {0, 0}, pa_c[2] = {0, 0}, pb_c[2] = {0, 0};
-  uint32_t cnt_c[2] = {0, 0};
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    if (c < nsplit) {
-      const int t = seg_at(a, L, c == 0 ? split_seg0 : split_seg1).tile;
-      const uint32_t u_first = (uint32_t)t * (uint32_t)a.ku;
-      tile_c[c] = t;
-      pa_c[c] = sk_owner(a, u_first);
-      pb_c[c] = sk_owner(a, u_first + (uint32_t)a.ku - 1);
-      for (int q0 = pa_c[c]; q0 <= pb_c[c]; q0 += 64) {
+      // participants and how many own split units (64 workgroups at a time)
+      const uint32_t u_first = (uint32_t)s.tile * (uint32_t)a.ku;
+      const int pa = sk_owner(a, u_first), pb = sk_owner(a, u_first + (uint32_t)a.ku - 1);
+      uint32_t cnt = 0;
+      for (int q0 = pa; q0 <= pb; q0 += 64) {
         const int q = q0 + lane;
-        cnt_c[c] += __popcll(__ballot(q <= pb_c[c] && part_slot(a, q, t) >= 0));
+        cnt += __popcll(__ballot(q <= pb && part_slot(a, q, s.tile) >= 0));
       }
+      if (c == 0) X.t0 = s.tile, X.pa0 = pa, X.pb0 = pb, cnt0 = cnt;
+      else X.t1 = s.tile, X.pa1 = pa, X.pb1 = pb, cnt1 = cnt;
     }
   }
+  if (X.n == 0) return X;
   __builtin_amdgcn_s_waitcnt(0);  // the slot stores are acknowledged
   // lane c counts this workgroup into split tile c; a workgroup owns the first
   // unit of at most one split tile, so the owner's index names the counter
   bool last = false;
-  if (lane < nsplit) {
-    const uint32_t c = lane == 0 ? cnt_c[0] : cnt_c[1];
-    const int pa = lane == 0 ? pa_c[0] : pa_c[1];
+  if (lane < X.n) {
+    const uint32_t c = lane == 0 ? cnt0 : cnt1;
+    const int pa = lane == 0 ? X.pa0 : X.pa1;
     last = __builtin_amdgcn_atomic_inc32(&a.ctr[pa], c - 1, __ATOMIC_RELAXED, "agent") == c - 1;
   }
-  const uint64_t last_mask = __ballot(last);
-  for (int c = 0; c < nsplit; ++c) {
-    if (!((last_mask >> c) & 1)) continue;
-    const int t = c == 0 ? tile_c[0] : tile_c[1];
-    const int pa = c == 0 ? pa_c[0] : pa_c[1], pb = c == 0 ? pb_c[0] : pb_c[1];
+  X.last = __ballot(last);
+  return X;
+}
+
+template <int MM, int ROWS, int TR>
+__device__ __forceinline__ void xch_end(const GemmParams& a, HelperLds<MM, ROWS>& h, const Xch& X, int lane) {
+  constexpr int LPR = 64 / TR;
+  constexpr int MJ = (MM + LPR - 1) / LPR;
+  constexpr int QC = MJ <= 4 ? 16 : MJ <= 8 ? 8 : 4;  // slots loaded per round trip
+  const int r = lane % TR, mq = lane / TR;
+  for (int c = 0; c < X.n; ++c) {
+    if (!((X.last >> c) & 1)) continue;
+    const int t = c == 0 ? X.t0 : X.t1;
+    const int pa = c == 0 ? X.pa0 : X.pa1, pb = c == 0 ? X.pb0 : X.pb1;
     const int n0 = t * TR;
     float v[MJ];
 #pragma unroll
@@ -518,7 +591,7 @@ __device__ __forceinline__ void finish(const GemmParams& a, HelperLds<MM, ROWS>&
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
         const int m = mq + LPR * j;
-        if (m < a.m) emit(a, n0 + r, m, v[j], h.kbest);
+        if (m < a.m) emit(a, n0 + r, m, (v[j] - h.cn[c][m][r]) + h.cp[c][m][r], h.kbest);
       }
     }
   }
@@ -546,50 +619,61 @@ __device__ __forceinline__ void finish_argmax(const GemmParams& a, HelperLds<MM,
   }
 }
 
-// Correction targets: segments [j0, j1) of the list (at most three).
-template <int MM, int ROWS, bool XT>
-__device__ __forceinline__ void corrections_for(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L,
-                                                int j0, int j1, int tile_rows, int lane) {
-  const int nt = j1 - j0;
-  if (nt <= 0) return;
-  auto make = [&](int j) {
-    const Seg s = seg_at(a, L, j);
-    return Tgt{j % kSlots, s.tile * tile_rows, seg_rows(s, tile_rows), (uint32_t)s.k0 * kUnitCols,
-               (uint32_t)s.k1 * kUnitCols};
-  };
-  const Tgt z{0, 0, 0, 0, 0};
-  corrections<MM, ROWS, XT>(a, h, nt, make(j0), nt > 1 ? make(j0 + 1) : z, nt > 2 ? make(j0 + 2) : z, lane);
+// Correction target for segment j: its rows, over all columns.
+__device__ __forceinline__ Tgt seg_target(const GemmParams& a, const SegList& L, int j, int tile_rows) {
+  const Seg s = seg_at(a, L, j);
+  return Tgt{j % kSlots, s.tile * tile_rows, seg_rows(s, tile_rows), 0u, (uint32_t)a.ku * kUnitCols};
 }
 
-// The helper wave. It first gathers the corrections of the first three
-// segments (at kernel start), then takes each
-// segment's partial sums as the streaming waves leave them: the split
-// segments (streamed first) are finished together through one exchange, the
-// whole-tile segments one by one; corrections of later segments are gathered
-// as their slots free up.
+// The helper wave. Split segments (streamed first): it loads the scales and
+// row pointers of the first three segments, takes the split segments' sums
+// as soon as they are left in LDS, stores them scaled in the exchange slots,
+// then gathers the escape corrections of all three segments while the whole
+// tiles stream, and finishes the split tiles it was last on. Whole-tile
+// segments then follow one by one: take, apply (A 2^(E_n-127) - CN) + CP,
+// write; corrections of later segments are gathered as their slots free up.
 template <int MM, int ROWS, int TR, class Compact>
 __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int p,
                                        int lane, Compact&& compact) {
+  constexpr bool XT = TR == 16;  // the MFMA kernel reads the transposed activations
   if (lane < MM) h.kbest[lane] = 0ull;
   const int n = L.n;
+  auto take = [&](int i) {
+    lds_wait_geq(&h.ready[i & 1], (uint32_t)kStreamWaves * (uint32_t)(i / 2 + 1));
+    compact(i & 1, i % kSlots, seg_at(a, L, i));
+    lds_set(&h.consumed, (uint32_t)(i + 1));
+  };
+  const Tgt z{0, 0, 0, 0, 0};
   int corr_end = 0;  // segments [0, corr_end) have their corrections
-  for (int b0 = 0; b0 < n;) {
+  int b0 = 0;
+  if (L.nsk > 0) {
+    const int nt = min(n, kSlots);
+    const Tgt t0 = seg_target(a, L, 0, TR), t1 = nt > 1 ? seg_target(a, L, 1, TR) : z,
+              t2 = nt > 2 ? seg_target(a, L, 2, TR) : z;
+    corr_rows(a, h, nt, t0, t1, t2, lane);
+    for (int i = 0; i < L.nsk; ++i) {
+      take(i);
+      scale_only(a, h, i, TR, lane);
+    }
+    const Xch X = xch_begin<MM, ROWS, TR>(a, h, L, p, lane);
+    corr_list<MM, ROWS, XT>(a, h, nt, t0, t1, t2, lane);
+    corr_end = nt;
+    xch_end<MM, ROWS, TR>(a, h, X, lane);
+    b0 = L.nsk;
+  }
+  for (; b0 < n; ++b0) {
     // segments before b0 are finished, so the slots of b0 .. b0 + 2 are free
     const int ce = min(n, b0 + kSlots);
     if (corr_end < ce) {
-      corrections_for<MM, ROWS, TR == 16>(a, h, L, corr_end, ce, TR, lane);
+      const int nt = ce - corr_end;
+      corrections<MM, ROWS, XT>(a, h, nt, seg_target(a, L, corr_end, TR),
+                                nt > 1 ? seg_target(a, L, corr_end + 1, TR) : z,
+                                nt > 2 ? seg_target(a, L, corr_end + 2, TR) : z, lane);
       corr_end = ce;
     }
-    // the split segments together (one exchange), else one whole-tile segment
-    const int b1 = b0 < L.nsk ? L.nsk : b0 + 1;
-    for (int i = b0; i < b1; ++i) {
-      lds_wait_geq(&h.ready[i & 1], (uint32_t)kStreamWaves * (uint32_t)(i / 2 + 1));
-      compact(i & 1, i % kSlots, seg_at(a, L, i));
-      lds_set(&h.consumed, (uint32_t)(i + 1));
-    }
-    for (int i = b0; i < b1; ++i) apply(a, h, i % kSlots, seg_rows(seg_at(a, L, i), TR), lane);
-    finish<MM, ROWS, TR>(a, h, L, p, b0, b1 - b0, lane);
-    b0 = b1;
+    take(b0);
+    apply(a, h, b0 % kSlots, seg_rows(seg_at(a, L, b0), TR), lane);
+    emit_whole<MM, ROWS, TR>(a, h, L, b0, lane);
   }
   if (a.mode == kModeArgmax) finish_argmax(a, h, p, lane);
 }
@@ -629,11 +713,17 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t*
   __syncthreads();
   if (wave == kStreamWaves) {
     auto compact = [&](int buf, int sl, const Seg&) {
+      // all reads before any write (the compiler would wait on each access)
+      float t[kStreamWaves][M];
+#pragma unroll
+      for (int w = 0; w < kStreamWaves; ++w)
+#pragma unroll
+        for (int m = 0; m < M; ++m) t[w][m] = sh.part[buf][w][m][lane];
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        float v = sh.part[buf][0][m][lane];
+        float v = t[0][m];
 #pragma unroll
-        for (int w = 1; w < kStreamWaves; ++w) v += sh.part[buf][w][m][lane];
+        for (int w = 1; w < kStreamWaves; ++w) v += t[w][m];
         sh.h.cv[sl][m][lane] = v;
       }
     };
@@ -708,7 +798,7 @@ struct MfmaStage {
 
 template <int MT>
 struct MfmaLds {
-  float part[2][kStreamWaves][kMfmaR<MT>][MT][4][64];  // C of each tile and m-tile, double-buffered
+  alignas(16) float part[2][kStreamWaves][kMfmaR<MT>][MT][4][64];  // C of each tile and m-tile, double-buffered
   HelperLds<MT * 16, kMfmaR<MT> * 16> h;
 };
 
@@ -797,14 +887,24 @@ __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
       if (rr < s.rg * 16) {
         const int j = rr >> 4, row = rr & 15, i = row & 3, lb = (row >> 2) * 16;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+          // the four waves' 16 values of this m-tile, all read before any write
+          float t[kStreamWaves][16];
+#pragma unroll
+          for (int w = 0; w < kStreamWaves; ++w)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 v = *reinterpret_cast<const float4*>(&sh.part[buf][w][j][mt][i][lb + 4 * q]);
+              t[w][4 * q] = v.x, t[w][4 * q + 1] = v.y, t[w][4 * q + 2] = v.z, t[w][4 * q + 3] = v.w;
+            }
 #pragma unroll
           for (int mm = 0; mm < 16; ++mm) {
-            float v = sh.part[buf][0][j][mt][i][lb + mm];
+            float v = t[0][mm];
 #pragma unroll
-            for (int w = 1; w < kStreamWaves; ++w) v += sh.part[buf][w][j][mt][i][lb + mm];
+            for (int w = 1; w < kStreamWaves; ++w) v += t[w][mm];
             sh.h.cv[sl][mt * 16 + mm][rr] = v;
           }
+        }
       }
     };
     helper<MT * 16, R * 16, kMfmaTileRows>(a, sh.h, L, p, lane, compact);
@@ -828,26 +928,35 @@ __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
 }
 
 // ============================================================== activation transpose
-// x [M, K] -> xt [K, MM]: 64 columns per workgroup through LDS, both sides
-// read and written in rows.
+// x [M, K] -> xt [K, MM]: 32 columns per workgroup through LDS, read in
+// 16-byte pieces along rows of x and written in 16-byte pieces along rows of xt.
 __global__ __launch_bounds__(256) void k_xpose(const uint16_t* __restrict__ x, int64_t ldx, int M, int MM,
                                                uint16_t* __restrict__ xt) {
-  __shared__ uint16_t t[64][65];
-  const int c0 = blockIdx.x * 64;
-  for (int i = threadIdx.x; i < MM * 64; i += 256) {
-    const int m = i >> 6, c = i & 63;
-    t[m][c] = m < M ? x[(int64_t)m * ldx + c0 + c] : (uint16_t)0;
+  __shared__ uint16_t t[64][32 + 8];  // [m][column], rows padded to keep 16-byte alignment
+  const int c0 = blockIdx.x * 32;
+  // MM rows x 4 pieces of 8 columns
+  for (int i = threadIdx.x; i < MM * 4; i += 256) {
+    const int m = i >> 2, q = i & 3;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (m < M) v = *reinterpret_cast<const uint4*>(x + (int64_t)m * ldx + c0 + 8 * q);
+    *reinterpret_cast<uint4*>(&t[m][8 * q]) = v;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * MM; i += 256) {
-    const int c = i / MM, m = i - c * MM;
-    xt[(int64_t)(c0 + c) * MM + m] = t[m][c];
+  // 32 columns x MM / 8 pieces of 8 activation rows
+  const int pr = MM / 8;
+  for (int i = threadIdx.x; i < 32 * pr; i += 256) {
+    const int c = i / pr, q = i - c * pr;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)t[8 * q + 2 * j][c] | (uint32_t)t[8 * q + 2 * j + 1][c] << 16;
+    *reinterpret_cast<uint4*>(xt + (int64_t)(c0 + c) * MM + 8 * q) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
 hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, uint16_t* xt, hipStream_t s) {
-  if (mm > 64 || M > mm || K % 64 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_xpose, dim3(K / 64), dim3(256), 0, s, x, ldx, M, mm, xt);
+  if (mm > 64 || mm % 16 != 0 || M > mm || K % 32 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_xpose, dim3(K / 32), dim3(256), 0, s, x, ldx, M, mm, xt);
   return hipGetLastError();
 }
 
