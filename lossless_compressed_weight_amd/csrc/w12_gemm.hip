@@ -27,12 +27,11 @@
 // bias (w = w' 2^(E_n - 127)); CN = sum of x * placeholder and CP = sum of x *
 // exact value over the segment's escapes. The value is (A 2^(E_n-127) - CN) + CP.
 //
-// Split tiles: each workgroup stores its scaled sum A 2^(E_n-127) in a fixed
-// slot (2p for its first split tile, 2p+1 for its second) and counts itself
-// in the tile's counter; the last to arrive adds the slots in workgroup order
-// (so the result does not depend on arrival order), applies the tile's escape
-// corrections over all its columns - (sum - CN) + CP - and writes the tile.
-// Counters wrap back to zero, so every call leaves them zeroed for the next one.
+// Split tiles: each workgroup stores its segment value in a fixed slot (2p for
+// its first split tile, 2p+1 for its second) and counts itself in the tile's
+// counter; the last to arrive adds the slots in workgroup order (so the result
+// does not depend on arrival order) and writes the tile. Counters wrap back to
+// zero, so every call leaves them zeroed for the next one.
 #include "w12_internal.h"
 
 namespace w12 {
@@ -383,17 +382,18 @@ __device__ __forceinline__ void corr_rows(const GemmParams& a, HelperLds<MM, ROW
 }
 
 template <int MM, int ROWS, bool XT>
-__device__ __forceinline__ void corr_list(const GemmParams& a, HelperLds<MM, ROWS>& h, int nt, Tgt g0t, Tgt g1t,
-                                          Tgt g2t, int lane) {
+__device__ __forceinline__ void corr_list(const GemmParams& a, HelperLds<MM, ROWS>& h, int t_first, int nt, Tgt g0t,
+                                          Tgt g1t, Tgt g2t, int lane) {
   if (!a.fix) return;
   // the targets' entries as one index space [0, J): target t holds
   // [pre_t, pre_t + size_t), its entries [E0_t, E0_t + size_t)
+  // (targets before t_first count as empty)
   const uint32_t E00 = __builtin_amdgcn_readfirstlane(h.rp[0][0]);
-  const uint32_t E10 = __builtin_amdgcn_readfirstlane(h.rp[0][g0t.rows]);
+  const uint32_t E10 = t_first > 0 ? E00 : __builtin_amdgcn_readfirstlane(h.rp[0][g0t.rows]);
   const uint32_t E01 = nt > 1 ? __builtin_amdgcn_readfirstlane(h.rp[1][0]) : 0u;
-  const uint32_t E11 = nt > 1 ? __builtin_amdgcn_readfirstlane(h.rp[1][g1t.rows]) : 0u;
+  const uint32_t E11 = nt > 1 && t_first <= 1 ? __builtin_amdgcn_readfirstlane(h.rp[1][g1t.rows]) : E01;
   const uint32_t E02 = nt > 2 ? __builtin_amdgcn_readfirstlane(h.rp[2][0]) : 0u;
-  const uint32_t E12 = nt > 2 ? __builtin_amdgcn_readfirstlane(h.rp[2][g2t.rows]) : 0u;
+  const uint32_t E12 = nt > 2 ? __builtin_amdgcn_readfirstlane(h.rp[2][g2t.rows]) : E02;
   const uint32_t pre1 = E10 - E00, pre2 = pre1 + (E11 - E01), J = pre2 + (E12 - E02);
   for (uint32_t b0 = 0; b0 < J; b0 += kEscList) {
     uint2 e[kEscLoad];
@@ -431,7 +431,7 @@ template <int MM, int ROWS, bool XT>
 __device__ __forceinline__ void corrections(const GemmParams& a, HelperLds<MM, ROWS>& h, int nt, Tgt g0t, Tgt g1t,
                                             Tgt g2t, int lane) {
   corr_rows(a, h, nt, g0t, g1t, g2t, lane);
-  corr_list<MM, ROWS, XT>(a, h, nt, g0t, g1t, g2t, lane);
+  corr_list<MM, ROWS, XT>(a, h, 0, nt, g0t, g1t, g2t, lane);
 }
 
 // Rows of a segment.
@@ -459,24 +459,6 @@ __device__ __forceinline__ void apply(const GemmParams& a, HelperLds<MM, ROWS>& 
   }
 }
 
-// value = A * scale for every (row, m) of slot sl (a split segment: its
-// corrections are applied once, to the tile's sum).
-template <int MM, int ROWS>
-__device__ __forceinline__ void scale_only(const GemmParams& a, HelperLds<MM, ROWS>& h, int sl, int rows, int lane) {
-  if (lane < rows && lane < ROWS) {
-    const float s = h.scale[sl][lane];
-#pragma unroll
-    for (int m0 = 0; m0 < MM; m0 += 8) {
-      float c[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = h.cv[sl][m0 + j < MM ? m0 + j : MM - 1][lane];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (m0 + j < MM && m0 + j < a.m) h.cv[sl][m0 + j][lane] = c[j] * s;
-    }
-  }
-}
-
 // Whole-tile segment si (slot si % 3): its finished values are written out.
 template <int MM, int ROWS, int TR>
 __device__ __forceinline__ void emit_whole(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int si,
@@ -490,11 +472,10 @@ __device__ __forceinline__ void emit_whole(const GemmParams& a, HelperLds<MM, RO
   }
 }
 
-// The exchange of a workgroup's split segments (0 .. nsk-1, slots 0 and 1).
-// Begin: store this workgroup's scaled sums A 2^(E_n-127) in its fixed slots,
-// then count it into each tile. End: for the tiles it was last on, add all
-// slots in workgroup order and apply the tile's escape corrections over all
-// its columns: value = (sum - CN) + CP. In the exchange a lane serves row
+// The exchange of one or two of a workgroup's split segments [b0, b1).
+// Begin: store this workgroup's segment values in its fixed slots, then count
+// it into each tile. End: for the tiles it was last on, add all slots in
+// workgroup order and write the tile. In the exchange a lane serves row
 // lane % TR and activation rows lane / TR + (64 / TR) j.
 struct Xch {
   int n;              // split segments
@@ -505,21 +486,22 @@ struct Xch {
 
 template <int MM, int ROWS, int TR>
 __device__ __forceinline__ Xch xch_begin(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int p,
-                                         int lane) {
+                                         int b0, int b1, int lane) {
   constexpr int LPR = 64 / TR;
   constexpr int MJ = (MM + LPR - 1) / LPR;
   const int r = lane % TR, mq = lane / TR;
-  Xch X{L.nsk, 0, 0, 0, 0, 0, 0, 0ull};
+  Xch X{b1 - b0, 0, 0, 0, 0, 0, 0, 0ull};
   uint32_t cnt0 = 0, cnt1 = 0;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     if (c < X.n) {
-      const Seg s = seg_at(a, L, c);
+      const int si = b0 + c, sl = si % kSlots;
+      const Seg s = seg_at(a, L, si);
       float* dst = a.part + (int64_t)(2 * p + s.part) * MM * TR;
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
         const int m = mq + LPR * j;
-        if (m < a.m) store_shared(&dst[m * TR + r], h.cv[c][m][r]);
+        if (m < a.m) store_shared(&dst[m * TR + r], h.cv[sl][m][r]);
       }
       // participants and how many own split units (64 workgroups at a time)
       const uint32_t u_first = (uint32_t)s.tile * (uint32_t)a.ku;
@@ -591,7 +573,7 @@ __device__ __forceinline__ void xch_end(const GemmParams& a, HelperLds<MM, ROWS>
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
         const int m = mq + LPR * j;
-        if (m < a.m) emit(a, n0 + r, m, (v[j] - h.cn[c][m][r]) + h.cp[c][m][r], h.kbest);
+        if (m < a.m) emit(a, n0 + r, m, v[j], h.kbest);
       }
     }
   }
@@ -619,61 +601,65 @@ __device__ __forceinline__ void finish_argmax(const GemmParams& a, HelperLds<MM,
   }
 }
 
-// Correction target for segment j: its rows, over all columns.
+// Correction target for segment j: its rows and columns.
 __device__ __forceinline__ Tgt seg_target(const GemmParams& a, const SegList& L, int j, int tile_rows) {
   const Seg s = seg_at(a, L, j);
-  return Tgt{j % kSlots, s.tile * tile_rows, seg_rows(s, tile_rows), 0u, (uint32_t)a.ku * kUnitCols};
+  return Tgt{j % kSlots, s.tile * tile_rows, seg_rows(s, tile_rows), (uint32_t)s.k0 * kUnitCols,
+             (uint32_t)s.k1 * kUnitCols};
 }
 
-// The helper wave. Split segments (streamed first): it loads the scales and
-// row pointers of the first three segments, takes the split segments' sums
-// as soon as they are left in LDS, stores them scaled in the exchange slots,
-// then gathers the escape corrections of all three segments while the whole
-// tiles stream, and finishes the split tiles it was last on. Whole-tile
-// segments then follow one by one: take, apply (A 2^(E_n-127) - CN) + CP,
-// write; corrections of later segments are gathered as their slots free up.
+// The helper wave. It finishes the segments in stream order (two split
+// segments together when the second is short): corrections of the segment,
+// take its partial sums as the streaming waves leave them, apply
+// (A 2^(E_n-127) - CN) + CP, then write a whole tile or start the exchange of
+// a split one; while the exchange's stores and count are in flight it gathers
+// the corrections of the next segments (whose slots are free by then).
+constexpr int kMergeUnits = 8;  // a split segment this short joins the previous one's exchange
+
 template <int MM, int ROWS, int TR, class Compact>
 __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int p,
                                        int lane, Compact&& compact) {
   constexpr bool XT = TR == 16;  // the MFMA kernel reads the transposed activations
   if (lane < MM) h.kbest[lane] = 0ull;
   const int n = L.n;
-  auto take = [&](int i) {
-    lds_wait_geq(&h.ready[i & 1], (uint32_t)kStreamWaves * (uint32_t)(i / 2 + 1));
-    compact(i & 1, i % kSlots, seg_at(a, L, i));
-    lds_set(&h.consumed, (uint32_t)(i + 1));
-  };
   const Tgt z{0, 0, 0, 0, 0};
   int corr_end = 0;  // segments [0, corr_end) have their corrections
-  int b0 = 0;
-  if (L.nsk > 0) {
-    const int nt = min(n, kSlots);
-    const Tgt t0 = seg_target(a, L, 0, TR), t1 = nt > 1 ? seg_target(a, L, 1, TR) : z,
-              t2 = nt > 2 ? seg_target(a, L, 2, TR) : z;
-    corr_rows(a, h, nt, t0, t1, t2, lane);
-    for (int i = 0; i < L.nsk; ++i) {
-      take(i);
-      scale_only(a, h, i, TR, lane);
-    }
-    const Xch X = xch_begin<MM, ROWS, TR>(a, h, L, p, lane);
-    corr_list<MM, ROWS, XT>(a, h, nt, t0, t1, t2, lane);
-    corr_end = nt;
-    xch_end<MM, ROWS, TR>(a, h, X, lane);
-    b0 = L.nsk;
-  }
-  for (; b0 < n; ++b0) {
-    // segments before b0 are finished, so the slots of b0 .. b0 + 2 are free
-    const int ce = min(n, b0 + kSlots);
-    if (corr_end < ce) {
-      const int nt = ce - corr_end;
+  // corrections of segments [corr_end, j1), three at a time
+  auto corr_upto = [&](int j1) {
+    while (corr_end < j1) {
+      const int nt = min(3, j1 - corr_end);
       corrections<MM, ROWS, XT>(a, h, nt, seg_target(a, L, corr_end, TR),
                                 nt > 1 ? seg_target(a, L, corr_end + 1, TR) : z,
                                 nt > 2 ? seg_target(a, L, corr_end + 2, TR) : z, lane);
-      corr_end = ce;
+      corr_end += nt;
     }
-    take(b0);
-    apply(a, h, b0 % kSlots, seg_rows(seg_at(a, L, b0), TR), lane);
-    emit_whole<MM, ROWS, TR>(a, h, L, b0, lane);
+  };
+  // the segments finished together from b0: two split ones when the second is short
+  auto group_end = [&](int b0) {
+    if (b0 + 1 < L.nsk) {
+      const Seg s1 = seg_at(a, L, b0 + 1);
+      if (s1.k1 - s1.k0 <= kMergeUnits) return b0 + 2;
+    }
+    return b0 + 1;
+  };
+  corr_upto(group_end(0));
+  for (int b0 = 0; b0 < n;) {
+    const bool split = b0 < L.nsk;
+    const int b1 = group_end(b0);  // (its corrections were gathered ahead)
+    for (int i = b0; i < b1; ++i) {
+      lds_wait_geq(&h.ready[i & 1], (uint32_t)kStreamWaves * (uint32_t)(i / 2 + 1));
+      compact(i & 1, i % kSlots, seg_at(a, L, i));
+      lds_set(&h.consumed, (uint32_t)(i + 1));
+      apply(a, h, i % kSlots, seg_rows(seg_at(a, L, i), TR), lane);
+    }
+    Xch X{0, 0, 0, 0, 0, 0, 0, 0ull};
+    if (split) X = xch_begin<MM, ROWS, TR>(a, h, L, p, b0, b1, lane);
+    else emit_whole<MM, ROWS, TR>(a, h, L, b0, lane);
+    // segments before b1 are done with their slots: those of b1 .. b1 + 2 are
+    // free (this also covers the next group)
+    corr_upto(min(n, b1 + kSlots));
+    if (split) xch_end<MM, ROWS, TR>(a, h, X, lane);
+    b0 = b1;
   }
   if (a.mode == kModeArgmax) finish_argmax(a, h, p, lane);
 }
