@@ -155,8 +155,9 @@ int w12_decode(const w12_matrix* m, uint16_t* w_out, void* stream);
 
 /* Exact W12 GEMM (section 4.1, Figure 5b): y[M, N] = x[M, K] W^T with fp32
  * accumulation, escapes fixed up exactly before the output rounding.
- * x: BF16, row stride ldx >= K elements, 16-byte aligned rows.
- * y: BF16 or fp32 (y_dtype), row stride ldy >= N elements.
+ * x: BF16, row stride ldx >= K elements (a multiple of 8, at most 2^25),
+ *    16-byte aligned rows.
+ * y: BF16 or fp32 (y_dtype), row stride ldy >= N elements (below 2^31).
  * 1 <= M <= 64: M < 16 runs the wavefront GEMV kernel, M >= 16 the MFMA kernel.
  * ws: w12_workspace_bytes(W12_OP_GEMM, n, k, M) bytes (device). */
 int w12_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,

@@ -47,8 +47,8 @@ int check_gemm_args(const w12_matrix* m, const void* x, int64_t M, int64_t ldx, 
   if (s != W12_OK) return s;
   if (M < 1 || M > W12_MAX_M) return W12_E_M_RANGE;
   if (!x || !y) return W12_E_INVALID_ARG;
-  if (ldx < m->k || ldx % 8 != 0 || !aligned16(x)) return W12_E_INVALID_ARG;
-  if (ldy < m->n) return W12_E_INVALID_ARG;
+  if (ldx < m->k || ldx % 8 != 0 || ldx > ((int64_t)1 << 25) || !aligned16(x)) return W12_E_INVALID_ARG;
+  if (ldy < m->n || ldy > INT32_MAX) return W12_E_INVALID_ARG;
   if (y_dtype != W12_BF16 && y_dtype != W12_F32) return W12_E_INVALID_ARG;
   return W12_OK;
 }

@@ -6,12 +6,14 @@
 // deterministic. Section 4.3: the Q pass reads only the 8-bit view.
 // Appendix E: the LM head in W12, here fused with a per-row argmax.
 //
-// Work: the matrix is a sequence of row tiles (64 rows for the GEMV kernel,
-// 16 for the MFMA kernel), each a sequence of units of 256 columns. With P
-// workgroups (one per compute unit) and T tiles, workgroup p owns the whole
-// tiles [p D, (p+1) D), D = T / P, and an even share of the units of the
-// remaining T - P D tiles (stream-K). A segment is the units of one tile (or
-// of a group of whole tiles) that a workgroup processes in one pass.
+// Work: rows come in 16-row blocks and columns in units of 256. A whole tile
+// is GB blocks (64 rows; 32 for the MFMA kernel beyond 32 activation rows).
+// With P workgroups (one per compute unit) and T whole tiles, workgroup p owns
+// the tiles [p D, (p+1) D), D = T / P. The rows left after the P D tiles are
+// cut into split tiles of TB blocks (GB, or a single block when few rows are
+// left, so that each split tile has few sharers) and their units are shared
+// evenly by all workgroups (stream-K). A segment is the units of one tile that
+// a workgroup processes in one pass.
 //
 // Each workgroup runs four streaming waves and one helper wave. The streaming
 // waves only stream records and activations: per segment they leave their
@@ -53,15 +55,16 @@ __device__ __forceinline__ uint32_t div_floor(uint64_t x, uint32_t y) {
   return q;
 }
 
+// Split units are numbered from the first split tile: unit u is column unit
+// u % ku of split tile u / ku.
 // First split unit of workgroup q (q in [0, P]).
 __device__ __forceinline__ uint32_t sk_start(const GemmParams& a, int q) {
-  return (uint32_t)a.sk_base + div_floor((uint64_t)q * (uint64_t)a.sk_units, (uint32_t)a.P);
+  return div_floor((uint64_t)q * (uint64_t)a.sk_units, (uint32_t)a.P);
 }
 
 // Workgroup owning split unit u.
 __device__ __forceinline__ int sk_owner(const GemmParams& a, uint32_t u) {
-  const uint64_t v = u - (uint32_t)a.sk_base;
-  return (int)div_floor((v + 1) * (uint64_t)a.P + (uint64_t)a.sk_units - 1, (uint32_t)a.sk_units) - 1;
+  return (int)div_floor(((uint64_t)u + 1) * (uint64_t)a.P + (uint64_t)a.sk_units - 1, (uint32_t)a.sk_units) - 1;
 }
 
 // Workgroup q's slot for split tile t: 2q if t is its first split tile, 2q+1
@@ -73,52 +76,65 @@ __device__ __forceinline__ int part_slot(const GemmParams& a, int q, int t) {
   return 2 * q + ((s >= t0 && s < t0 + (uint32_t)a.ku) ? 0 : 1);
 }
 
+// First row of split tile t.
+template <int TB>
+__device__ __forceinline__ int split_row0(const GemmParams& a, int t) {
+  return a.sk_row0 + t * TB * 16;
+}
+
 struct Seg {
-  int tile;    // first tile
-  int rg;      // tiles (whole-tile groups of the MFMA kernel; 1 otherwise)
-  int k0, k1;  // units [k0, k1) of each tile
-  int part;    // split tile: 0 or 1 (which of this workgroup's split tiles); -1: whole
+  int row0;    // first row
+  int rg;      // 16-row blocks (fewer than the tile's only at the end of the matrix)
+  int k0, k1;  // units [k0, k1)
+  int tile;    // split tile index (whole tile: -1)
+  int part;    // which of this workgroup's split tiles, 0 or 1 (whole tile: -1)
 };
 
-// The segments of workgroup p: nsk split ones (shorter first), then whole
-// tiles in groups of at most rmax.
+// The segments of workgroup p: nsk split ones (shorter first), then its D
+// whole tiles.
 struct SegList {
   int n, nsk;
   Seg sk0, sk1;
-  int dp0, D, rmax;
+  int dp0;
 };
 
-__device__ __forceinline__ SegList seg_list(const GemmParams& a, int p, int rmax) {
+template <int TB>
+__device__ __forceinline__ Seg split_seg(const GemmParams& a, int t, int k0, int k1, int part) {
+  const int r0 = split_row0<TB>(a, t);
+  return Seg{r0, min(TB, (a.n - r0) >> 4), k0, k1, t, part};
+}
+
+template <int TB>
+__device__ __forceinline__ SegList seg_list(const GemmParams& a, int p) {
   SegList L;
-  L.rmax = rmax;
-  L.D = a.dp;
   L.dp0 = p * a.dp;
   L.nsk = 0;
-  L.sk0 = L.sk1 = Seg{0, 1, 0, 0, 0};
+  L.sk0 = L.sk1 = Seg{0, 0, 0, 0, -1, -1};
   const uint32_t s0 = sk_start(a, p), s1 = sk_start(a, p + 1);
   if (s1 > s0) {
-    const int ta = (int)div_floor(s0, (uint32_t)a.ku), tb = (int)div_floor(s1 - 1, (uint32_t)a.ku);
-    const uint32_t ua = (uint32_t)ta * (uint32_t)a.ku, ub = (uint32_t)tb * (uint32_t)a.ku;
-    const Seg A{ta, 1, (int)(s0 - ua), ta == tb ? (int)(s1 - ua) : a.ku, 0};
-    if (ta == tb) {
+    const int ta = (int)div_floor(s0, (uint32_t)a.ku), tz = (int)div_floor(s1 - 1, (uint32_t)a.ku);
+    const uint32_t ua = (uint32_t)ta * (uint32_t)a.ku, uz = (uint32_t)tz * (uint32_t)a.ku;
+    const Seg A = split_seg<TB>(a, ta, (int)(s0 - ua), ta == tz ? (int)(s1 - ua) : a.ku, 0);
+    if (ta == tz) {
       L.nsk = 1;
       L.sk0 = A;
     } else {
-      const Seg B{tb, 1, 0, (int)(s1 - ub), 1};
+      const Seg B = split_seg<TB>(a, tz, 0, (int)(s1 - uz), 1);
       L.nsk = 2;
       const bool b_first = (B.k1 - B.k0) < (A.k1 - A.k0);
       L.sk0 = b_first ? B : A;
       L.sk1 = b_first ? A : B;
     }
   }
-  L.n = L.nsk + (a.dp + rmax - 1) / rmax;
+  L.n = L.nsk + a.dp;
   return L;
 }
 
+template <int GB>
 __device__ __forceinline__ Seg seg_at(const GemmParams& a, const SegList& L, int i) {
   if (i < L.nsk) return i == 0 ? L.sk0 : L.sk1;
-  const int j = i - L.nsk;
-  return Seg{L.dp0 + j * L.rmax, min(L.rmax, L.D - j * L.rmax), 0, a.ku, -1};
+  const int r0 = (L.dp0 + i - L.nsk) * GB * 16;
+  return Seg{r0, min(GB, (a.n - r0) >> 4), 0, a.ku, -1, -1};
 }
 
 // -------------------------------------------------------------- outputs
@@ -139,22 +155,81 @@ __device__ __forceinline__ unsigned long long load_shared(const unsigned long lo
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void emit(const GemmParams& a, int n, int m, float v, unsigned long long* kbest) {
-  if (a.mode == kModeStore) {
-    if (a.y_f32) reinterpret_cast<float*>(a.y)[(int64_t)m * a.ldy + n] = v;
-    else reinterpret_cast<uint16_t*>(a.y)[(int64_t)m * a.ldy + n] = f32_to_bf16_rne(v);
+// One lane's outputs: v[j] is activation row m0 + MS j at output column n.
+// The bound, address and stride live in vector registers (the helper is short
+// of scalar ones; kept there, each store would first reload them), and the
+// dtype branch sits outside the per-value loop.
+template <int J, int MS>
+__device__ __forceinline__ void store_values(const GemmParams& a, int n, int m0, const float (&v)[J]) {
+  const int mend = (int)opaque_vgpr((uint32_t)a.m);
+  const uint32_t ld = opaque_vgpr((uint32_t)a.ldy);  // ldy < 2^31 (checked by the API)
+  const uint64_t step = (uint64_t)ld * (uint64_t)MS;
+  const uint64_t off = (uint64_t)ld * (uint64_t)(uint32_t)m0 + (uint64_t)(uint32_t)n;
+  if (a.y_f32) {
+    float* y = reinterpret_cast<float*>(a.y) + off;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (m0 + MS * j < mend) y[step * j] = v[j];
   } else {
-    atomicMax(&kbest[m], argmax_key(v, (uint32_t)n));
+    uint16_t* y = reinterpret_cast<uint16_t*>(a.y) + off;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (m0 + MS * j < mend) y[step * j] = f32_to_bf16_rne(v[j]);
+  }
+}
+
+__device__ __forceinline__ unsigned long long max_u64(unsigned long long x, unsigned long long y) {
+  return x > y ? x : y;
+}
+
+// Lane i takes the key of lane (i - CTRL + 0x120) mod 16 of its 16-lane row (row rotate).
+template <int CTRL>
+__device__ __forceinline__ unsigned long long row_ror_u64(unsigned long long k) {
+  const int lo = (int)(uint32_t)k, hi = (int)(uint32_t)(k >> 32);
+  const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+  const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+  return (unsigned long long)h << 32 | l;
+}
+
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long k, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), l);
+  return (unsigned long long)hi << 32 | lo;
+}
+
+// Argmax: lane m of the helper keeps kb, the largest key of activation row m
+// seen so far. argmax_absorb folds in one key per lane (0: none); each group
+// of G lanes (G = 64, 32 or 16) holds keys of one activation row, m0 + g for
+// group g. Rotations by 1, 2, 4 and 8 leave every lane of a 16-lane row with
+// the row's largest key. All lanes must be active.
+template <int G>
+__device__ __forceinline__ void argmax_absorb(unsigned long long& kb, unsigned long long key, int m0, int lane) {
+  key = max_u64(key, row_ror_u64<0x121>(key));
+  key = max_u64(key, row_ror_u64<0x122>(key));
+  key = max_u64(key, row_ror_u64<0x124>(key));
+  key = max_u64(key, row_ror_u64<0x128>(key));
+  const unsigned long long g0 = readlane_u64(key, 0), g1 = readlane_u64(key, 16), g2 = readlane_u64(key, 32),
+                           g3 = readlane_u64(key, 48);
+  if constexpr (G == 64) {
+    if (lane == m0) kb = max_u64(kb, max_u64(max_u64(g0, g1), max_u64(g2, g3)));
+  } else if constexpr (G == 32) {
+    const int d = lane - m0;
+    const unsigned long long g = d == 0 ? max_u64(g0, g1) : max_u64(g2, g3);
+    if (d >= 0 && d < 2) kb = max_u64(kb, g);
+  } else {
+    const int d = lane - m0;
+    const unsigned long long g = d == 0 ? g0 : d == 1 ? g1 : d == 2 ? g2 : g3;
+    if (d >= 0 && d < 4) kb = max_u64(kb, g);
   }
 }
 
 // -------------------------------------------------------------- escapes
-// The helper gathers a segment's escape corrections in three memory round
-// trips whatever the rows' escape counts (up to a few hundred entries): the
-// row pointers of the segment's rows; all their entries at once (lane = entry),
-// filtered to the segment's columns and appended to a list in LDS; then, with
-// lane = activation row, the activations of 32 or 64 listed entries at a time,
-// summed per row in column order.
+// The helper gathers the escape corrections of up to three segments in three
+// memory round trips for up to a few hundred entries: the row pointers of the
+// segments' rows; all their entries at once (lane = entry), filtered to the
+// segments' columns and appended to a list in LDS; then the activations of the
+// listed entries (lane = entry again), whose products are added to the rows'
+// sums in column order.
 constexpr int kEscLoad = 8;    // entries per lane per load round trip
 constexpr int kEscList = 64 * kEscLoad;
 
@@ -205,13 +280,10 @@ struct HelperLds {
   float cn[kSlots][MM][ROWS];
   float cp[kSlots][MM][ROWS];
   float scale[kSlots][ROWS];
-  unsigned long long kbest[MM];
   uint32_t rp[3][ROWS + 1];                   // row pointers of each target's rows
   alignas(16) uint32_t ecol[kEscList];        // listed entries: column,
   uint32_t ebits[kEscList];                   // original BF16 | placeholder << 16,
   uint32_t erow[kEscList];                    // target * 256 + row
-  alignas(16) float xs[64][20];  // gathered activations [entry][activation row], rows padded
-  float eph[64], eex[64];    // placeholder and exact value of a pass's entries
   int poff[64];              // exchange: slots of a chunk of participants
   uint32_t ready[2];  // streaming waves done with the partial buffer (cumulative)
   uint32_t consumed;  // segments whose partial sums the helper has taken
@@ -244,96 +316,86 @@ __device__ __forceinline__ int rp_row(const uint32_t* rp, int rows, uint32_t j) 
 
 // Add the listed entries [0, n) to the corrections, 64 at a time with
 // lane = entry. Entries come sorted by (target, row, column), so each row's
-// entries of a pass are a run of lanes: the activations of all entries are
-// gathered at once (16 activation rows per round trip) and parked in LDS,
-// then the first lane of each run sums the run in column order and adds it
-// to the row's LDS sums (a run split across passes adds its parts in order).
+// entries of a pass are a run of lanes; in round k the k-th entry of every run
+// adds its products to its row's sums, so no two lanes of a round touch the
+// same sums and every row's sums grow in column order (a run split across
+// passes continues in the next pass). The activations of PB passes' entries
+// are gathered in one round trip and stay in registers.
 template <int MM, int ROWS, bool XT>
 __device__ __forceinline__ void esc_list_apply(const GemmParams& a, HelperLds<MM, ROWS>& h, int n, int slot0,
                                                int slot1, int slot2, int lane) {
   // target t's slot is bits 4t .. 4t+3 (arithmetic, not a select, so the
   // slot stays an index into the LDS arrays)
   const uint32_t slots = (uint32_t)slot0 | (uint32_t)slot1 << 4 | (uint32_t)slot2 << 8;
-  for (int e0 = 0; e0 < n; e0 += 64) {
-    const int ne = min(64, n - e0);
-    const bool live = lane < ne;
-    const int e = e0 + (live ? lane : 0);
-    const uint32_t col = live ? h.ecol[e] : 0u, bits = live ? h.ebits[e] : 0u;
-    const uint32_t tr = live ? h.erow[e] : 0xFFFFFFFFu;
-    const bool head = live && (lane == 0 || h.erow[e - 1] != tr);
-    int len = 0;
-    if (head) {
-      len = 1;
-      while (lane + len < ne && h.erow[e + len] == tr) ++len;
-    }
-    h.eph[lane] = esc_placeholder(a, bits);
-    h.eex[lane] = bf16_to_f32(bits & 0xFFFFu);
-    const uint32_t sl = (slots >> (4 * ((tr >> 8) & 3u))) & 15u, r = tr & 255u;
-    // XT: the entry's activations for all rows, one line of the transposed copy
-    constexpr int XW = XT ? MM / 2 : 1;
-    uint32_t xw[XW];
-    if constexpr (XT) {
-      const uint4* xp = reinterpret_cast<const uint4*>(a.xt + (size_t)col * MM);
+  // activation loads per lane and pass; the loads of PB passes go out together
+  // (within a register budget of LB loads)
+  constexpr int LP = XT ? MM / 8 : MM;
+  constexpr int LB = XT && MM > 32 ? 8 : 16;
+  constexpr int PB = LP >= LB ? 1 : (LB / LP > kEscLoad ? kEscLoad : LB / LP);
+  constexpr int C = MM < 16 ? MM : 16;  // activation rows per batch of LDS reads
+  for (int e00 = 0; e00 < n; e00 += 64 * PB) {
+    // XT: the entry's activations for all rows, one line of the transposed
+    // copy (rows past M are zero there); otherwise one load per row (MM = M)
+    uint4 xq[PB][XT ? MM / 8 : 1];
+    uint16_t xg[PB][XT ? 1 : MM];
 #pragma unroll
-      for (int i = 0; i < MM / 8; ++i) {
-        const uint4 v = xp[i];
-        xw[4 * i] = v.x, xw[4 * i + 1] = v.y, xw[4 * i + 2] = v.z, xw[4 * i + 3] = v.w;
-      }
-    }
-#pragma unroll
-    for (int m0 = 0; m0 < (XT ? MM : 64); m0 += 16) {
-      if (m0 >= a.m) break;
-      float xv[16];
+    for (int pp = 0; pp < PB; ++pp) {
+      const int e = e00 + 64 * pp + lane;
+      const uint32_t col = e < n ? h.ecol[e] : 0u;
       if constexpr (XT) {
+        const uint4* xp = reinterpret_cast<const uint4*>(a.xt + (size_t)col * MM);
 #pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          const uint32_t w = xw[(m0 + j) / 2];
-          xv[j] = bf16_to_f32(w & 0xFFFFu);
-          xv[j + 1] = bf16_to_f32(w >> 16);
-        }
+        for (int i = 0; i < MM / 8; ++i) xq[pp][i] = xp[i];
       } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int m = (m0 + j < a.m) ? m0 + j : 0;
-          xv[j] = bf16_to_f32(a.x[(int64_t)m * a.ldx + col]);
-        }
+        for (int m = 0; m < MM; ++m) xg[pp][m] = a.x[(int64_t)(m < a.m ? m : 0) * a.ldx + col];
       }
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(&h.xs[lane][4 * q]) =
-            make_float4(xv[4 * q], xv[4 * q + 1], xv[4 * q + 2], xv[4 * q + 3]);
-      if (head) {
-        float sn[16], sp[16];
+    for (int pp = 0; pp < PB; ++pp) {
+      const int e0 = e00 + 64 * pp;
+      if (e0 < n) {
+        const int ne = min(64, n - e0);
+        const bool live = lane < ne;
+        const int e = e0 + (live ? lane : 0);
+        const uint32_t bits = h.ebits[e];
+        const uint32_t tr = live ? h.erow[e] : 0xFFFFFFFFu;
+        const uint32_t tp = lane > 0 ? h.erow[max(e - 1, 0)] : 0xFFFFFFFEu;
+        const bool head = live && (lane == 0 || tp != tr);
+        // position in the run: lanes since the closest head at or below this lane
+        const uint64_t below = __ballot(head) & (lane == 63 ? ~0ull : (2ull << lane) - 1ull);
+        const int pos = below ? lane - (63 - __clzll(below)) : 0;
+        const float ph = esc_placeholder(a, bits), ex = bf16_to_f32(bits & 0xFFFFu);
+        const uint32_t sl = (slots >> (4 * ((tr >> 8) & 3u))) & 15u, r = live ? tr & 255u : 0u;
+        float xv[MM];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sn[j] = sp[j] = 0.f;
-        for (int k = 0; k < len; ++k) {
-          const float ph = h.eph[lane + k], ex = h.eex[lane + k];
-          float xk[16];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(&h.xs[lane + k][4 * q]);
-            xk[4 * q] = v.x, xk[4 * q + 1] = v.y, xk[4 * q + 2] = v.z, xk[4 * q + 3] = v.w;
-          }
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            sn[j] = fmaf(xk[j], ph, sn[j]);
-            sp[j] = fmaf(xk[j], ex, sp[j]);
+        for (int m = 0; m < MM; m += 2) {
+          if constexpr (XT) {
+            const uint4 q = xq[pp][m / 8];
+            const int w = (m % 8) / 2;
+            const uint32_t u = w == 0 ? q.x : w == 1 ? q.y : w == 2 ? q.z : q.w;
+            xv[m] = bf16_to_f32(u & 0xFFFFu);
+            xv[m + 1] = bf16_to_f32(u >> 16);
+          } else {
+            xv[m] = bf16_to_f32(xg[pp][m]);
+            if (m + 1 < MM) xv[m + 1] = bf16_to_f32(xg[pp][m + 1 < MM ? m + 1 : m]);
           }
         }
-        // all reads before any write (the compiler cannot tell the LDS
-        // addresses apart and would otherwise wait on each access)
-        float on[16], op[16];
+        for (int k = 0; __ballot(live && pos >= k) != 0; ++k) {
+          if (live && pos == k) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int m = m0 + j < MM ? m0 + j : MM - 1;
-          on[j] = h.cn[sl][m][r];
-          op[j] = h.cp[sl][m][r];
-        }
+            for (int m0 = 0; m0 < MM; m0 += C) {
+              // all reads before any write (the compiler cannot tell the LDS
+              // addresses apart and would otherwise wait on each access)
+              float on[C], op[C];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          if (m0 + j < a.m && m0 + j < MM) {
-            h.cn[sl][m0 + j][r] = on[j] + sn[j];
-            h.cp[sl][m0 + j][r] = op[j] + sp[j];
+              for (int j = 0; j < C; ++j) on[j] = h.cn[sl][m0 + j][r], op[j] = h.cp[sl][m0 + j][r];
+#pragma unroll
+              for (int j = 0; j < C; ++j) {
+                h.cn[sl][m0 + j][r] = fmaf(xv[m0 + j], ph, on[j]);
+                h.cp[sl][m0 + j][r] = fmaf(xv[m0 + j], ex, op[j]);
+              }
+            }
           }
         }
       }
@@ -434,41 +496,45 @@ __device__ __forceinline__ void corrections(const GemmParams& a, HelperLds<MM, R
   corr_list<MM, ROWS, XT>(a, h, 0, nt, g0t, g1t, g2t, lane);
 }
 
-// Rows of a segment.
-__device__ __forceinline__ int seg_rows(const Seg& s, int tile_rows) { return s.rg * tile_rows; }
-
-// value = (A * scale - CN) + CP for every (row, m) of slot sl.
-// (Each chunk of 8 is read before it is written: the compiler cannot tell
-// the LDS addresses apart and would otherwise wait on every access.)
-template <int MM, int ROWS>
-__device__ __forceinline__ void apply(const GemmParams& a, HelperLds<MM, ROWS>& h, int sl, int rows, int lane) {
-  if (lane < rows && lane < ROWS) {
-    const float s = h.scale[sl][lane];
+// Finished values (A * scale - CN) + CP of row r, activation rows m0 + MS j,
+// from slot sl. All LDS reads come first (the compiler cannot tell the LDS
+// addresses apart and would otherwise wait on every access).
+template <int J, int MS, int MM, int ROWS>
+__device__ __forceinline__ void seg_values(const HelperLds<MM, ROWS>& h, int sl, int r, int m0, float (&v)[J]) {
+  const float s = h.scale[sl][r];
+  float c[J], cn[J], cp[J];
 #pragma unroll
-    for (int m0 = 0; m0 < MM; m0 += 8) {
-      float c[8], cn[8], cp[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int m = m0 + j < MM ? m0 + j : MM - 1;
-        c[j] = h.cv[sl][m][lane], cn[j] = h.cn[sl][m][lane], cp[j] = h.cp[sl][m][lane];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (m0 + j < MM && m0 + j < a.m) h.cv[sl][m0 + j][lane] = (c[j] * s - cn[j]) + cp[j];
-    }
+  for (int j = 0; j < J; ++j) {
+    const int m = m0 + MS * j < MM ? m0 + MS * j : MM - 1;
+    c[j] = h.cv[sl][m][r], cn[j] = h.cn[sl][m][r], cp[j] = h.cp[sl][m][r];
   }
+#pragma unroll
+  for (int j = 0; j < J; ++j) v[j] = (c[j] * s - cn[j]) + cp[j];
 }
 
-// Whole-tile segment si (slot si % 3): its finished values are written out.
-template <int MM, int ROWS, int TR>
+// Whole-tile segment si (slot si % 3), lane = row: its outputs or argmax keys.
+template <int MM, int ROWS>
 __device__ __forceinline__ void emit_whole(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int si,
-                                           int lane) {
-  const Seg s = seg_at(a, L, si);
-  const int sl = si % kSlots, rows = seg_rows(s, TR), n0 = s.tile * TR;
-  if (lane < rows && lane < ROWS && n0 + lane < a.n) {
+                                           int lane, unsigned long long& kb) {
+  const Seg s = seg_at<ROWS / 16>(a, L, si);
+  const int sl = si % kSlots, n0 = s.row0;
+  const bool valid = lane < s.rg * 16 && lane < ROWS;
+  const int r = lane < ROWS ? lane : ROWS - 1;
+  constexpr int C = MM < 16 ? MM : 16;
+#pragma unroll 1
+  for (int m0 = 0; m0 < MM; m0 += C) {
+    if (m0 < a.m) {
+      float v[C];
+      seg_values<C, 1>(h, sl, r, m0, v);
+      if (a.mode == kModeStore) {
+        if (valid) store_values<C, 1>(a, n0 + lane, m0, v);
+      } else {
 #pragma unroll
-    for (int m = 0; m < MM; ++m)
-      if (m < a.m) emit(a, n0 + lane, m, h.cv[sl][m][lane], h.kbest);
+        for (int j = 0; j < C; ++j)
+          if (m0 + j < a.m)
+            argmax_absorb<64>(kb, valid ? argmax_key(v[j], (uint32_t)(n0 + lane)) : 0ull, m0 + j, lane);
+      }
+    }
   }
 }
 
@@ -476,7 +542,8 @@ __device__ __forceinline__ void emit_whole(const GemmParams& a, HelperLds<MM, RO
 // Begin: store this workgroup's segment values in its fixed slots, then count
 // it into each tile. End: for the tiles it was last on, add all slots in
 // workgroup order and write the tile. In the exchange a lane serves row
-// lane % TR and activation rows lane / TR + (64 / TR) j.
+// lane % TS and activation rows lane / TS + (64 / TS) j (TS: rows of a split
+// tile).
 struct Xch {
   int n;              // split segments
   int t0, t1;         // their tiles
@@ -484,24 +551,30 @@ struct Xch {
   uint64_t last;      // bit c: this workgroup finishes tile c
 };
 
-template <int MM, int ROWS, int TR>
+template <int MM, int ROWS, int TS>
 __device__ __forceinline__ Xch xch_begin(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int p,
                                          int b0, int b1, int lane) {
-  constexpr int LPR = 64 / TR;
+  constexpr int LPR = 64 / TS;
   constexpr int MJ = (MM + LPR - 1) / LPR;
-  const int r = lane % TR, mq = lane / TR;
+  const int r = lane % TS, mq = lane / TS;
   Xch X{b1 - b0, 0, 0, 0, 0, 0, 0, 0ull};
   uint32_t cnt0 = 0, cnt1 = 0;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     if (c < X.n) {
       const int si = b0 + c, sl = si % kSlots;
-      const Seg s = seg_at(a, L, si);
-      float* dst = a.part + (int64_t)(2 * p + s.part) * MM * TR;
+      const Seg s = seg_at<ROWS / 16>(a, L, si);
+      float* dst = a.part + (int64_t)(2 * p + s.part) * MM * TS;
+      constexpr int JC = MJ < 8 ? MJ : 8;  // values per batch of LDS reads
 #pragma unroll
-      for (int j = 0; j < MJ; ++j) {
-        const int m = mq + LPR * j;
-        if (m < a.m) store_shared(&dst[m * TR + r], h.cv[sl][m][r]);
+      for (int j0 = 0; j0 < MJ; j0 += JC) {
+        float v[JC];
+        seg_values<JC, LPR>(h, sl, r, mq + LPR * j0, v);
+#pragma unroll
+        for (int j = 0; j < JC; ++j) {
+          const int m = mq + LPR * (j0 + j);
+          if (m < a.m) store_shared(&dst[m * TS + r], v[j]);
+        }
       }
       // participants and how many own split units (64 workgroups at a time)
       const uint32_t u_first = (uint32_t)s.tile * (uint32_t)a.ku;
@@ -529,51 +602,58 @@ __device__ __forceinline__ Xch xch_begin(const GemmParams& a, HelperLds<MM, ROWS
   return X;
 }
 
-template <int MM, int ROWS, int TR>
-__device__ __forceinline__ void xch_end(const GemmParams& a, HelperLds<MM, ROWS>& h, const Xch& X, int lane) {
-  constexpr int LPR = 64 / TR;
+template <int MM, int ROWS, int TS>
+__device__ __forceinline__ void xch_end(const GemmParams& a, HelperLds<MM, ROWS>& h, const Xch& X, int lane,
+                                        unsigned long long& kb) {
+  constexpr int LPR = 64 / TS;
   constexpr int MJ = (MM + LPR - 1) / LPR;
-  constexpr int QC = MJ <= 4 ? 16 : MJ <= 8 ? 8 : 4;  // slots loaded per round trip
-  const int r = lane % TR, mq = lane / TR;
+  constexpr int JC = MJ < 8 ? MJ : 8;       // values per lane per pass
+  constexpr int QC = JC <= 4 ? 16 : 8;      // slots loaded per round trip
+  const int r = lane % TS, mq = lane / TS;
   for (int c = 0; c < X.n; ++c) {
     if (!((X.last >> c) & 1)) continue;
     const int t = c == 0 ? X.t0 : X.t1;
     const int pa = c == 0 ? X.pa0 : X.pa1, pb = c == 0 ? X.pb0 : X.pb1;
-    const int n0 = t * TR;
-    float v[MJ];
+    const int n0 = split_row0<TS / 16>(a, t);
+#pragma unroll 1
+    for (int j0 = 0; j0 < MJ && LPR * j0 < a.m; j0 += JC) {
+      float v[JC];
 #pragma unroll
-    for (int j = 0; j < MJ; ++j) v[j] = 0.f;
-    bool started = false;  // adds start from the first slot (keeps the sign of a zero sum)
-    for (int q0 = pa; q0 <= pb; q0 += 64) {
-      const int nq = min(64, pb - q0 + 1);
-      h.poff[lane] = lane < nq ? part_slot(a, q0 + lane, t) : -1;
-      for (int i0 = 0; i0 < nq; i0 += QC) {
-        float tv[QC][MJ];
-        int sl[QC];
+      for (int j = 0; j < JC; ++j) v[j] = 0.f;
+      bool started = false;  // adds start from the first slot (keeps the sign of a zero sum)
+      for (int q0 = pa; q0 <= pb; q0 += 64) {
+        const int nq = min(64, pb - q0 + 1);
+        h.poff[lane] = lane < nq ? part_slot(a, q0 + lane, t) : -1;
+        for (int i0 = 0; i0 < nq; i0 += QC) {
+          float tv[QC][JC];
+          int sl[QC];
 #pragma unroll
-        for (int u = 0; u < QC; ++u) {
-          sl[u] = i0 + u < nq ? h.poff[i0 + u] : -1;
-          const int64_t base = (int64_t)max(sl[u], 0) * MM * TR;
+          for (int u = 0; u < QC; ++u) {
+            sl[u] = i0 + u < nq ? h.poff[i0 + u] : -1;
+            const int64_t base = (int64_t)max(sl[u], 0) * MM * TS;
 #pragma unroll
-          for (int j = 0; j < MJ; ++j) {
-            const int m = mq + LPR * j;
-            tv[u][j] = (sl[u] >= 0 && m < a.m) ? load_shared(&a.part[base + m * TR + r]) : 0.f;
+            for (int j = 0; j < JC; ++j) {
+              const int m = mq + LPR * (j0 + j);
+              tv[u][j] = (sl[u] >= 0 && m < a.m) ? load_shared(&a.part[base + m * TS + r]) : 0.f;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < QC; ++u) {
+            if (sl[u] < 0) continue;
+#pragma unroll
+            for (int j = 0; j < JC; ++j) v[j] = started ? v[j] + tv[u][j] : tv[u][j];
+            started = true;
           }
         }
-#pragma unroll
-        for (int u = 0; u < QC; ++u) {
-          if (sl[u] < 0) continue;
-#pragma unroll
-          for (int j = 0; j < MJ; ++j) v[j] = started ? v[j] + tv[u][j] : tv[u][j];
-          started = true;
-        }
       }
-    }
-    if (n0 + r < a.n) {
+      if (a.mode == kModeStore) {
+        if (n0 + r < a.n) store_values<JC, LPR>(a, n0 + r, mq + LPR * j0, v);
+      } else {
 #pragma unroll
-      for (int j = 0; j < MJ; ++j) {
-        const int m = mq + LPR * j;
-        if (m < a.m) emit(a, n0 + r, m, v[j], h.kbest);
+        for (int j = 0; j < JC; ++j) {
+          const bool ok = n0 + r < a.n && mq + LPR * (j0 + j) < a.m;
+          argmax_absorb<TS>(kb, ok ? argmax_key(v[j], (uint32_t)(n0 + r)) : 0ull, LPR * (j0 + j), lane);
+        }
       }
     }
   }
@@ -581,9 +661,8 @@ __device__ __forceinline__ void xch_end(const GemmParams& a, HelperLds<MM, ROWS>
 
 // Argmax mode: publish this workgroup's best key per activation row; the last
 // workgroup to finish reduces all of them into idx / max.
-template <int MM, int ROWS>
-__device__ __forceinline__ void finish_argmax(const GemmParams& a, HelperLds<MM, ROWS>& h, int p, int lane) {
-  if (lane < a.m) store_shared(&a.keys[(int64_t)p * a.m + lane], h.kbest[lane]);
+__device__ __forceinline__ void finish_argmax(const GemmParams& a, int p, int lane, unsigned long long kb) {
+  if (lane < a.m) store_shared(&a.keys[(int64_t)p * a.m + lane], kb);
   __builtin_amdgcn_s_waitcnt(0);
   bool last = false;
   if (lane == 0)
@@ -602,25 +681,29 @@ __device__ __forceinline__ void finish_argmax(const GemmParams& a, HelperLds<MM,
 }
 
 // Correction target for segment j: its rows and columns.
-__device__ __forceinline__ Tgt seg_target(const GemmParams& a, const SegList& L, int j, int tile_rows) {
-  const Seg s = seg_at(a, L, j);
-  return Tgt{j % kSlots, s.tile * tile_rows, seg_rows(s, tile_rows), (uint32_t)s.k0 * kUnitCols,
+template <int GB>
+__device__ __forceinline__ Tgt seg_target(const GemmParams& a, const SegList& L, int j) {
+  const Seg s = seg_at<GB>(a, L, j);
+  return Tgt{j % kSlots, s.row0, s.rg * 16, (uint32_t)s.k0 * kUnitCols,
              (uint32_t)s.k1 * kUnitCols};
 }
 
 // The helper wave. It finishes the segments in stream order (two split
 // segments together when the second is short): corrections of the segment,
-// take its partial sums as the streaming waves leave them, apply
-// (A 2^(E_n-127) - CN) + CP, then write a whole tile or start the exchange of
-// a split one; while the exchange's stores and count are in flight it gathers
-// the corrections of the next segments (whose slots are free by then).
+// take its partial sums as the streaming waves leave them, then write a whole
+// tile's values (A 2^(E_n-127) - CN) + CP or start the exchange of a split
+// one; while the exchange's stores and count are in flight it gathers the
+// corrections of the next segments (whose slots are free by then).
 constexpr int kMergeUnits = 8;  // a split segment this short joins the previous one's exchange
 
-template <int MM, int ROWS, int TR, class Compact>
+template <int MM, int ROWS, int TS, bool XT, class Compact>
 __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int p,
                                        int lane, Compact&& compact) {
-  constexpr bool XT = TR == 16;  // the MFMA kernel reads the transposed activations
-  if (lane < MM) h.kbest[lane] = 0ull;
+  // Instruction issue priority over the streaming waves: the helper's work is
+  // a chain of short dependent steps, the streaming waves' is not.
+  __builtin_amdgcn_s_setprio(3);
+  constexpr int GB = ROWS / 16;  // 16-row blocks of a whole tile
+  unsigned long long kb = 0ull;  // argmax: lane m's best key of activation row m
   const int n = L.n;
   const Tgt z{0, 0, 0, 0, 0};
   int corr_end = 0;  // segments [0, corr_end) have their corrections
@@ -628,40 +711,41 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
   auto corr_upto = [&](int j1) {
     while (corr_end < j1) {
       const int nt = min(3, j1 - corr_end);
-      corrections<MM, ROWS, XT>(a, h, nt, seg_target(a, L, corr_end, TR),
-                                nt > 1 ? seg_target(a, L, corr_end + 1, TR) : z,
-                                nt > 2 ? seg_target(a, L, corr_end + 2, TR) : z, lane);
+      corrections<MM, ROWS, XT>(a, h, nt, seg_target<GB>(a, L, corr_end),
+                                nt > 1 ? seg_target<GB>(a, L, corr_end + 1) : z,
+                                nt > 2 ? seg_target<GB>(a, L, corr_end + 2) : z, lane);
       corr_end += nt;
     }
   };
   // the segments finished together from b0: two split ones when the second is short
   auto group_end = [&](int b0) {
     if (b0 + 1 < L.nsk) {
-      const Seg s1 = seg_at(a, L, b0 + 1);
+      const Seg s1 = seg_at<GB>(a, L, b0 + 1);
       if (s1.k1 - s1.k0 <= kMergeUnits) return b0 + 2;
     }
     return b0 + 1;
   };
-  corr_upto(group_end(0));
+  // the first three segments' corrections in one pass (the round trips cost
+  // the same for one target as for three)
+  corr_upto(min(n, kSlots));
   for (int b0 = 0; b0 < n;) {
     const bool split = b0 < L.nsk;
-    const int b1 = group_end(b0);  // (its corrections were gathered ahead)
+    const int b1 = group_end(b0);  // (their corrections were gathered ahead)
     for (int i = b0; i < b1; ++i) {
       lds_wait_geq(&h.ready[i & 1], (uint32_t)kStreamWaves * (uint32_t)(i / 2 + 1));
-      compact(i & 1, i % kSlots, seg_at(a, L, i));
+      compact(i & 1, i % kSlots, seg_at<GB>(a, L, i));
       lds_set(&h.consumed, (uint32_t)(i + 1));
-      apply(a, h, i % kSlots, seg_rows(seg_at(a, L, i), TR), lane);
     }
     Xch X{0, 0, 0, 0, 0, 0, 0, 0ull};
-    if (split) X = xch_begin<MM, ROWS, TR>(a, h, L, p, b0, b1, lane);
-    else emit_whole<MM, ROWS, TR>(a, h, L, b0, lane);
+    if (split) X = xch_begin<MM, ROWS, TS>(a, h, L, p, b0, b1, lane);
+    else emit_whole<MM, ROWS>(a, h, L, b0, lane, kb);
     // segments before b1 are done with their slots: those of b1 .. b1 + 2 are
     // free (this also covers the next group)
     corr_upto(min(n, b1 + kSlots));
-    if (split) xch_end<MM, ROWS, TR>(a, h, X, lane);
+    if (split) xch_end<MM, ROWS, TS>(a, h, X, lane, kb);
     b0 = b1;
   }
-  if (a.mode == kModeArgmax) finish_argmax(a, h, p, lane);
+  if (a.mode == kModeArgmax) finish_argmax(a, p, lane, kb);
 }
 
 // ============================================================== GEMV (M < 16)
@@ -694,7 +778,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t*
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x;
-  const SegList L = seg_list(a, p, 1);
+  const SegList L = seg_list<kGemvTileRows / 16>(a, p);
   if (threadIdx.x == 0) sh.h.ready[0] = sh.h.ready[1] = sh.h.consumed = 0;
   __syncthreads();
   if (wave == kStreamWaves) {
@@ -713,16 +797,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t*
         sh.h.cv[sl][m][lane] = v;
       }
     };
-    helper<M, kGemvTileRows, kGemvTileRows>(a, sh.h, L, p, lane, compact);
+    helper<M, kGemvTileRows, kGemvTileRows, false>(a, sh.h, L, p, lane, compact);
     return;
   }
   const uint32_t c3800 = opaque_vgpr(0x38003800u);
   const int64_t ldx = a.ldx;
   for (int i = 0; i < L.n; ++i) {
-    const Seg s = seg_at(a, L, i);
-    // lane -> row s.tile * 64 + lane; rows past N read block 0 of the tile
-    const int row = s.tile * kGemvTileRows + lane;
-    const uint8_t* tile_rec = a.rec + (int64_t)s.tile * 4 * a.kb * kRecBytes;
+    const Seg s = seg_at<kGemvTileRows / 16>(a, L, i);
+    // lane -> row s.row0 + lane; rows past N read block 0 of the tile
+    const int row = s.row0 + lane;
+    const uint8_t* tile_rec = a.rec + (int64_t)(s.row0 >> 4) * a.kb * kRecBytes;
     const uint32_t soff = row < a.n ? (uint32_t)(lane >> 4) * (uint32_t)(a.kb * kRecBytes) : 0u;
     const uint32_t voff = soff + (lane & 15) * 16, boff = soff + kViewBytes + (lane & 15) * 8;
     float acc[M];
@@ -766,12 +850,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t*
 // global memory. A wave's 1 KB view load of one 64-column chunk of a 16-row
 // block gives lane l row l%16 and columns 16 (l/16) .. +15: exactly the A
 // operands of two MFMAs; the B operands use the same lane -> column map.
-// A unit is 4 chunks (256 columns); streaming wave w takes chunk w. Whole
-// 16-row tiles are processed RG at a time so one activation load serves RG
-// tiles.
-constexpr int kMfmaTileRows = 16;
-
-// Tiles per group: 4 up to two m-tiles, 2 beyond (registers and LDS).
+// A unit is 4 chunks (256 columns); streaming wave w takes chunk w. A tile is
+// up to four 16-row blocks, so one activation load serves all of them.
+// 16-row blocks per tile: 4 up to two m-tiles, 2 beyond (registers and LDS).
 template <int MT>
 constexpr int kMfmaR = MT <= 2 ? 4 : 2;
 
@@ -788,7 +869,7 @@ struct MfmaLds {
   HelperLds<MT * 16, kMfmaR<MT> * 16> h;
 };
 
-// One segment: RG consecutive 16-row tiles starting at tile s, units [k0, k1).
+// One segment: the RG 16-row blocks starting at block s, units [k0, k1).
 template <int MT, int RG, bool Q>
 __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, int k1, int wave, int lane,
                                            float (*part)[kMfmaR<MT>][MT][4][64], int seg, const uint32_t* consumed) {
@@ -856,14 +937,15 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
       for (int i = 0; i < 4; ++i) part[wave][j][mt][i][lane] = acc[j][mt][i];
 }
 
-template <int MT, bool Q>
+// TB: 16-row blocks of a split tile (1 or R).
+template <int MT, bool Q, int TB>
 __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
   __shared__ MfmaLds<MT> sh;
   constexpr int R = kMfmaR<MT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x;
-  const SegList L = seg_list(a, p, R);
+  const SegList L = seg_list<TB>(a, p);
   if (threadIdx.x == 0) sh.h.ready[0] = sh.h.ready[1] = sh.h.consumed = 0;
   __syncthreads();
   if (wave == kStreamWaves) {
@@ -893,21 +975,22 @@ __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
         }
       }
     };
-    helper<MT * 16, R * 16, kMfmaTileRows>(a, sh.h, L, p, lane, compact);
+    helper<MT * 16, R * 16, TB * 16, true>(a, sh.h, L, p, lane, compact);
     return;
   }
   for (int i = 0; i < L.n; ++i) {
-    const Seg s = seg_at(a, L, i);
+    const Seg s = seg_at<R>(a, L, i);
+    const int b = s.row0 >> 4;  // first 16-row block
     if constexpr (R == 4) {
       switch (s.rg) {
-        case 1: mfma_group<MT, 1, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
-        case 2: mfma_group<MT, 2, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
-        case 3: mfma_group<MT, 3, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
-        default: mfma_group<MT, 4, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
+        case 1: mfma_group<MT, 1, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
+        case 2: mfma_group<MT, 2, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
+        case 3: mfma_group<MT, 3, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
+        default: mfma_group<MT, 4, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
       }
     } else {
-      if (s.rg == 1) mfma_group<MT, 1, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed);
-      else mfma_group<MT, 2, Q>(a, s.tile, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed);
+      if (s.rg == 1) mfma_group<MT, 1, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed);
+      else mfma_group<MT, 2, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed);
     }
     if (lane == 0) lds_add(&sh.h.ready[i & 1]);
   }
@@ -951,26 +1034,30 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t gr
   GemmPlan pl{};
   pl.mfma = (path == 2) || (path == 0 && m >= 16);
   pl.ku = (int)(k / kUnitCols);
-  if (pl.mfma) {
-    pl.tile_rows = kMfmaTileRows;
-    pl.tiles = (int)(n / kMfmaTileRows);
-  } else {
-    pl.tile_rows = kGemvTileRows;
-    pl.tiles = (int)((n + kGemvTileRows - 1) / kGemvTileRows);
-  }
-  pl.units = (int64_t)pl.tiles * pl.ku;
+  const int64_t mt = (m + 15) / 16;
+  pl.gb = pl.mfma ? (mt <= 2 ? kMfmaR<1> : kMfmaR<3>) : kGemvTileRows / 16;
+  const int64_t nb = n / 16;
+  const int64_t tiles = (nb + pl.gb - 1) / pl.gb;
   // One workgroup per compute unit: its four streaming waves keep enough
   // loads in flight, and the whole tiles go round-robin over the CUs.
   int64_t P = kNumCU;
   if (grid_override > 0) P = grid_override;
   if (P > kMaxGrid) P = kMaxGrid;
-  if (P > pl.units) P = pl.units;
+  if (P > tiles * pl.ku) P = tiles * pl.ku;
   if (P < 1) P = 1;
   pl.P = (int)P;
-  pl.dp = (int)(pl.tiles / P);
-  pl.sk_base = (int64_t)P * pl.dp * pl.ku;
-  pl.sk_units = pl.units - pl.sk_base;
-  const int64_t mm = pl.mfma ? ((m + 15) / 16) * 16 : m;
+  pl.dp = (int)(tiles / P);
+  const int64_t rem = nb - P * pl.dp * pl.gb;  // blocks left for the split tiles
+  // Split tiles are whole-tile sized when many rows are left (a few sharers
+  // each) and single blocks when few are: a tile shared by many workgroups
+  // would leave its last workgroup many partial sums to read. (The GEMV
+  // kernel's lanes are the 64 rows of a tile, so its tiles are always whole.)
+  pl.tb = (!pl.mfma || rem >= (P / 4) * pl.gb) ? pl.gb : 1;
+  pl.sk_row0 = (int)(P * pl.dp * pl.gb * 16);
+  pl.sk_tiles = (int)((rem + pl.tb - 1) / pl.tb);
+  pl.sk_units = (int64_t)pl.sk_tiles * pl.ku;
+  pl.tile_rows = pl.tb * 16;
+  const int64_t mm = pl.mfma ? mt * 16 : m;
   pl.ctr_bytes = kCounterBytes;
   pl.part_bytes = (size_t)(2 * P) * (size_t)mm * pl.tile_rows * sizeof(float);
   pl.key_bytes = (op == W12_OP_LMHEAD_ARGMAX) ? (size_t)P * (size_t)m * 8 : 0;
@@ -996,11 +1083,15 @@ static hipError_t launch_gemv_m(const GemmPlan& pl, const GemmParams& p, hipStre
 template <bool Q>
 static hipError_t launch_mfma_m(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   const dim3 grid(pl.P), block(kThreads);
+  const bool single = pl.tb == 1;
   switch ((p.m + 15) / 16) {
-    case 1: hipLaunchKernelGGL((k_mfma<1, Q>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_mfma<2, Q>), grid, block, 0, s, p); break;
-    case 3: hipLaunchKernelGGL((k_mfma<3, Q>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_mfma<4, Q>), grid, block, 0, s, p); break;
+#define W12_MFMA_CASE(MT)                                                                          \
+  case MT:                                                                                         \
+    if (single) hipLaunchKernelGGL((k_mfma<MT, Q, 1>), grid, block, 0, s, p);                      \
+    else hipLaunchKernelGGL((k_mfma<MT, Q, kMfmaR<MT>>), grid, block, 0, s, p);                     \
+    break;
+    W12_MFMA_CASE(1) W12_MFMA_CASE(2) W12_MFMA_CASE(3) W12_MFMA_CASE(4)
+#undef W12_MFMA_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1008,12 +1099,10 @@ static hipError_t launch_mfma_m(const GemmPlan& pl, const GemmParams& p, hipStre
 
 hipError_t launch_gemm(const GemmPlan& pl, GemmParams p, hipStream_t s, int* unsupported) {
   *unsupported = 0;
-  p.units = pl.units;
   p.ku = pl.ku;
-  p.tiles = pl.tiles;
   p.P = pl.P;
   p.dp = pl.dp;
-  p.sk_base = pl.sk_base;
+  p.sk_row0 = pl.sk_row0;
   p.sk_units = pl.sk_units;
   if (!pl.mfma && p.m > 16) {
     *unsupported = 1;

@@ -143,13 +143,11 @@ struct GemmParams {
   unsigned long long* keys;  // per-workgroup argmax keys [P][M]
   int32_t* idx;              // argmax outputs [M]
   float* maxv;               // argmax values [M] (may be null)
-  int64_t units;             // work units (tile x 256 columns) in the whole matrix
-  int64_t sk_base;           // first unit of the split (stream-K) tiles
-  int64_t sk_units;          // units of the split tiles
+  int64_t sk_units;          // units (split tile x 256 columns) of the split (stream-K) tiles
+  int sk_row0;               // first row of the split tiles
   int n, k;
   int kb;                    // records per 16-row block (K / 512)
-  int ku;                    // units per tile
-  int tiles;
+  int ku;                    // units per row of tiles (K / 256)
   int P;                     // workgroups
   int dp;                    // whole tiles per workgroup
   int m;                     // activation rows
@@ -172,12 +170,14 @@ hipError_t launch_validate(const w12_matrix* m, uint32_t* flag, hipStream_t s);
 struct GemmPlan {
   bool mfma;
   int P;
-  int tile_rows;
+  int gb;         // 16-row blocks of a whole tile
+  int tb;         // 16-row blocks of a split tile
+  int tile_rows;  // rows of a split tile (16 tb)
   int ku;
-  int tiles;
   int dp;
-  int64_t units;
-  int64_t sk_base, sk_units;
+  int sk_row0;
+  int sk_tiles;
+  int64_t sk_units;
   size_t ctr_bytes;
   size_t part_bytes;
   size_t key_bytes;
