@@ -158,7 +158,8 @@ int w12_decode(const w12_matrix* m, uint16_t* w_out, void* stream);
  * x: BF16, row stride ldx >= K elements (a multiple of 8, at most 2^25),
  *    16-byte aligned rows.
  * y: BF16 or fp32 (y_dtype), row stride ldy >= N elements (below 2^31).
- * 1 <= M <= 64: M < 16 runs the wavefront GEMV kernel, M >= 16 the MFMA kernel.
+ * 1 <= M <= 64: M == 1 runs the wavefront GEMV kernel, M >= 2 the MFMA kernel
+ * (M padded to a multiple of 16).
  * ws: w12_workspace_bytes(W12_OP_GEMM, n, k, M) bytes (device). */
 int w12_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,
              int y_dtype, void* ws, size_t ws_bytes, void* stream);
@@ -186,8 +187,8 @@ int w12_lmhead_argmax(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t
 int w12_validate(const w12_matrix* m, void* ws, size_t ws_bytes, void* stream);
 
 /* Test and tuning hooks (process-wide, not thread-safe; call before launching).
- * W12_TUNE_PATH: 0 = choose by M, 1 = force the GEMV kernel (M <= 15 only is
- *   the default range; forcing allows up to 16), 2 = force the MFMA kernel.
+ * W12_TUNE_PATH: 0 = choose by M, 1 = force the GEMV kernel (M <= 16),
+ *   2 = force the MFMA kernel.
  * W12_TUNE_GRID: workgroup count for the GEMM kernels (0 = default; at most
  *   4096 and at most the number of work units are used).
  * Changing W12_TUNE_GRID changes the fp32 summation order and the workspace

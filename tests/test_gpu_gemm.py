@@ -47,17 +47,37 @@ def test_gemm_matches_fp64_oracle(name, m):
     check_bf16(yb, yf, y64, f"{name} M={m}")
 
 
-@pytest.mark.parametrize("grid", [1, 3, 7, 64, 1000])
+@pytest.mark.parametrize("name", ["config0", "wide_k", "stress"])
+@pytest.mark.parametrize("m", [2, 5, 9, 15, 16])
+def test_forced_gemv_matches_oracle(name, m):
+    """The GEMV kernel runs M = 1 by default; forced, it serves every M up to 16."""
+    w = _mats()[name]
+    log(f"[gemv forced] {name} {w.shape} M={m}")
+    x = synth.make_activations(m, w.shape[1], seed=2000 + m)
+    mat = w12.encode(dev16(w))
+    w12.set_tuning(w12.TUNE_PATH, 1)
+    yf, yb = gemm_both(mat, dev16(x))
+    y64 = o.gemm_ref(x, w)
+    check_f32(yf, y64, f"gemv {name} M={m}")
+    check_bf16(yb, yf, y64, f"gemv {name} M={m}")
+
+
+@pytest.mark.parametrize("grid", [1, 3, 7, 15, 50, 1000])
 @pytest.mark.parametrize("m", [1, 5, 16, 40])
-def test_split_reduction_any_grid(grid, m):
+@pytest.mark.parametrize("path", [0, 1])
+def test_split_reduction_any_grid(grid, m, path):
     """Every workgroup count splits K differently (partial tiles reduced in a
-    fixed order); all must match the oracle."""
-    w = synth.workload_matrix(0, 0)[:256]
+    fixed order; at 15 workgroups the MFMA kernel's split tiles are single
+    16-row blocks); all must match the oracle. path 1 forces the GEMV kernel."""
+    if path == 1 and m > 16:
+        pytest.skip("the GEMV kernel serves M <= 16")
+    w = synth.workload_matrix(0, 0)
     x = synth.make_activations(m, 1024, seed=7 + m)
     mat = w12.encode(dev16(w))
     w12.set_tuning(w12.TUNE_GRID, grid)
+    w12.set_tuning(w12.TUNE_PATH, path)
     yf, yb = gemm_both(mat, dev16(x))
-    check_f32(yf, o.gemm_ref(x, w), f"grid={grid} M={m}")
+    check_f32(yf, o.gemm_ref(x, w), f"grid={grid} M={m} path={path}")
 
 
 def test_gemv_and_mfma_paths_agree_at_m16():
