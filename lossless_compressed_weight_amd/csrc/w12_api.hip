@@ -96,11 +96,14 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   p.fix = fix && m->n_esc > 0;
   p.q = op == W12_OP_GEMM_Q8;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // The MFMA kernel's escape fix-up reads the activations of an escape column
-  // for all rows at once from a transposed copy of x (one cache line instead
-  // of one per activation row).
+  // The MFMA kernel's escape fix-up needs the activations of each escape
+  // column for all rows. With many escapes per row it reads them from a
+  // transposed copy of x (one cache line per escape instead of one per
+  // activation row), at the price of one more kernel; with few it gathers
+  // them from x directly.
   p.xt = nullptr;
-  if (pl.mfma && p.fix && pl.xt_bytes > 0) {
+  const int64_t mm = ((M + 15) / 16) * 16;
+  if (pl.mfma && p.fix && pl.xt_bytes > 0 && m->n_esc * mm > kXtEscRowLines * m->n) {
     uint16_t* xt = reinterpret_cast<uint16_t*>(wsb + round256(pl.ctr_bytes) + round256(pl.part_bytes) +
                                                round256(pl.key_bytes));
     const hipError_t ex = launch_xpose(x, ldx, (int)M, (int)(((M + 15) / 16) * 16), (int)m->k, xt, st);

@@ -230,8 +230,11 @@ __device__ __forceinline__ void argmax_absorb(unsigned long long& kb, unsigned l
 // segments' columns and appended to a list in LDS; then the activations of the
 // listed entries (lane = entry again), whose products are added to the rows'
 // sums in column order.
-constexpr int kEscLoad = 8;    // entries per lane per load round trip
-constexpr int kEscList = 64 * kEscLoad;
+// Entries per lane per load round trip (fewer where registers are scarce,
+// beyond 32 activation rows), and the list capacity they fill.
+template <int MM>
+constexpr int kEscLoad = MM > 32 ? 8 : 16;
+constexpr int kEscList = 64 * 16;
 
 // The weight the main loop used for an escape: its placeholder, seen through
 // the Q view (low nibble 1000) in the Q pass.
@@ -320,22 +323,25 @@ __device__ __forceinline__ int rp_row(const uint32_t* rp, int rows, uint32_t j) 
 // adds its products to its row's sums, so no two lanes of a round touch the
 // same sums and every row's sums grow in column order (a run split across
 // passes continues in the next pass). The activations of PB passes' entries
-// are gathered in one round trip and stay in registers.
+// are gathered in one round trip and stay in registers: from the transposed
+// copy when there is one (XT, one line per entry), else from x (one load per
+// activation row).
 template <int MM, int ROWS, bool XT>
-__device__ __forceinline__ void esc_list_apply(const GemmParams& a, HelperLds<MM, ROWS>& h, int n, int slot0,
-                                               int slot1, int slot2, int lane) {
+__device__ __forceinline__ void esc_passes(const GemmParams& a, HelperLds<MM, ROWS>& h, int n, int slot0,
+                                           int slot1, int slot2, int lane) {
   // target t's slot is bits 4t .. 4t+3 (arithmetic, not a select, so the
   // slot stays an index into the LDS arrays)
   const uint32_t slots = (uint32_t)slot0 | (uint32_t)slot1 << 4 | (uint32_t)slot2 << 8;
   // activation loads per lane and pass; the loads of PB passes go out together
   // (within a register budget of LB loads)
   constexpr int LP = XT ? MM / 8 : MM;
-  constexpr int LB = XT && MM > 32 ? 8 : 16;
-  constexpr int PB = LP >= LB ? 1 : (LB / LP > kEscLoad ? kEscLoad : LB / LP);
+  constexpr int LB = XT ? (MM > 32 ? 8 : 16) : (MM > 32 ? 64 : 2 * MM > 16 ? 2 * MM : 16);
+  constexpr int PB = LP >= LB ? 1 : (LB / LP > kEscLoad<MM> ? kEscLoad<MM> : LB / LP);
   constexpr int C = MM < 16 ? MM : 16;  // activation rows per batch of LDS reads
   for (int e00 = 0; e00 < n; e00 += 64 * PB) {
     // XT: the entry's activations for all rows, one line of the transposed
-    // copy (rows past M are zero there); otherwise one load per row (MM = M)
+    // copy (rows past M are zero there); otherwise one load per row (rows
+    // past M repeat row 0; their sums are never used)
     uint4 xq[PB][XT ? MM / 8 : 1];
     uint16_t xg[PB][XT ? 1 : MM];
 #pragma unroll
@@ -403,6 +409,13 @@ __device__ __forceinline__ void esc_list_apply(const GemmParams& a, HelperLds<MM
   }
 }
 
+template <int MM, int ROWS, bool XT>
+__device__ __forceinline__ void esc_list_apply(const GemmParams& a, HelperLds<MM, ROWS>& h, int n, int slot0,
+                                               int slot1, int slot2, int lane) {
+  if (XT && a.xt) esc_passes<MM, ROWS, XT>(a, h, n, slot0, slot1, slot2, lane);
+  else esc_passes<MM, ROWS, false>(a, h, n, slot0, slot1, slot2, lane);
+}
+
 // A correction target: slot, rows row0 + r for r < rows, columns [c0, c1).
 struct Tgt {
   int slot, row0, rows;
@@ -457,12 +470,13 @@ __device__ __forceinline__ void corr_list(const GemmParams& a, HelperLds<MM, ROW
   const uint32_t E02 = nt > 2 ? __builtin_amdgcn_readfirstlane(h.rp[2][0]) : 0u;
   const uint32_t E12 = nt > 2 ? __builtin_amdgcn_readfirstlane(h.rp[2][g2t.rows]) : E02;
   const uint32_t pre1 = E10 - E00, pre2 = pre1 + (E11 - E01), J = pre2 + (E12 - E02);
-  for (uint32_t b0 = 0; b0 < J; b0 += kEscList) {
-    uint2 e[kEscLoad];
-    uint32_t gj[kEscLoad];
-    int tt[kEscLoad];
+  constexpr int EL = kEscLoad<MM>;
+  for (uint32_t b0 = 0; b0 < J; b0 += 64 * EL) {
+    uint2 e[EL];
+    uint32_t gj[EL];
+    int tt[EL];
 #pragma unroll
-    for (int k = 0; k < kEscLoad; ++k) {
+    for (int k = 0; k < EL; ++k) {
       const uint32_t g = b0 + 64 * k + lane;
       tt[k] = g < pre1 ? 0 : g < pre2 ? 1 : 2;
       gj[k] = g - pick3(tt[k], 0u, pre1, pre2) + pick3(tt[k], E00, E01, E02);
@@ -470,7 +484,7 @@ __device__ __forceinline__ void corr_list(const GemmParams& a, HelperLds<MM, ROW
     }
     int n = 0;
 #pragma unroll
-    for (int k = 0; k < kEscLoad; ++k) {
+    for (int k = 0; k < EL; ++k) {
       const int t = tt[k];
       const bool in = b0 + 64 * k + lane < J && e[k].x >= pick3(t, g0t.c0, g1t.c0, g2t.c0) &&
                       e[k].x < pick3(t, g0t.c1, g1t.c1, g2t.c1);
@@ -602,6 +616,22 @@ __device__ __forceinline__ Xch xch_begin(const GemmParams& a, HelperLds<MM, ROWS
   return X;
 }
 
+// Finished values of one lane (row n0 + r, activation rows m0 + LPR j): its
+// outputs, or its argmax keys.
+template <int J, int LPR, int TS>
+__device__ __forceinline__ void xch_out(const GemmParams& a, int n0, int r, int m0, const float (&v)[J], int lane,
+                                        unsigned long long& kb) {
+  if (a.mode == kModeStore) {
+    if (n0 + r < a.n) store_values<J, LPR>(a, n0 + r, m0, v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const bool ok = n0 + r < a.n && m0 + LPR * j < a.m;
+      argmax_absorb<TS>(kb, ok ? argmax_key(v[j], (uint32_t)(n0 + r)) : 0ull, m0 - lane / TS + LPR * j, lane);
+    }
+  }
+}
+
 template <int MM, int ROWS, int TS>
 __device__ __forceinline__ void xch_end(const GemmParams& a, HelperLds<MM, ROWS>& h, const Xch& X, int lane,
                                         unsigned long long& kb) {
@@ -609,12 +639,60 @@ __device__ __forceinline__ void xch_end(const GemmParams& a, HelperLds<MM, ROWS>
   constexpr int MJ = (MM + LPR - 1) / LPR;
   constexpr int JC = MJ < 8 ? MJ : 8;       // values per lane per pass
   constexpr int QC = JC <= 4 ? 16 : 8;      // slots loaded per round trip
+  constexpr int JP = MJ < 4 ? MJ : 4;       // pipelined passes: values per lane
+  constexpr int QP = MM > 32 ? 4 : 8;       // and slots (at most QP sharers)
   const int r = lane % TS, mq = lane / TS;
   for (int c = 0; c < X.n; ++c) {
     if (!((X.last >> c) & 1)) continue;
     const int t = c == 0 ? X.t0 : X.t1;
     const int pa = c == 0 ? X.pa0 : X.pa1, pb = c == 0 ? X.pb0 : X.pb1;
     const int n0 = split_row0<TS / 16>(a, t);
+    const int np = pb - pa + 1;  // workgroups that may hold units of the tile
+    if (MJ > JP && MM <= 32 && np <= QP) {
+      // Few sharers: their slots once, then passes over the activation rows
+      // with the next pass's loads in flight while this one is added up.
+      h.poff[lane] = lane < np ? part_slot(a, pa + lane, t) : -1;
+      int64_t base[QP];
+      bool has[QP];  // the workgroup holds units of the tile (the first one always does)
+#pragma unroll
+      for (int u = 0; u < QP; ++u) {
+        const int sl = u < np ? h.poff[u] : -1;
+        base[u] = (int64_t)max(sl, 0) * MM * TS;
+        has[u] = sl >= 0;
+      }
+      auto load = [&](float (&tv)[QP][JP], int j0) {
+#pragma unroll
+        for (int u = 0; u < QP; ++u)
+#pragma unroll
+          for (int j = 0; j < JP; ++j) {
+            const int m = mq + LPR * (j0 + j);
+            tv[u][j] = (has[u] && m < a.m) ? load_shared(&a.part[base[u] + m * TS + r]) : 0.f;
+          }
+      };
+      auto finish = [&](const float (&tv)[QP][JP], int j0) {
+        float v[JP];
+#pragma unroll
+        for (int j = 0; j < JP; ++j) v[j] = tv[0][j];
+#pragma unroll
+        for (int u = 1; u < QP; ++u)
+#pragma unroll
+          for (int j = 0; j < JP; ++j)
+            if (has[u]) v[j] += tv[u][j];
+        xch_out<JP, LPR, TS>(a, n0, r, mq + LPR * j0, v, lane, kb);
+      };
+      const int jend = min(MJ, (a.m + LPR - 1) / LPR);  // passes past M hold nothing
+      float ta[QP][JP], tb[QP][JP];
+      load(ta, 0);
+      for (int j0 = 0; j0 < jend; j0 += 2 * JP) {
+        if (j0 + JP < jend) load(tb, j0 + JP);
+        finish(ta, j0);
+        if (j0 + JP < jend) {
+          if (j0 + 2 * JP < jend) load(ta, j0 + 2 * JP);
+          finish(tb, j0 + JP);
+        }
+      }
+      continue;
+    }
 #pragma unroll 1
     for (int j0 = 0; j0 < MJ && LPR * j0 < a.m; j0 += JC) {
       float v[JC];
@@ -646,15 +724,7 @@ __device__ __forceinline__ void xch_end(const GemmParams& a, HelperLds<MM, ROWS>
           }
         }
       }
-      if (a.mode == kModeStore) {
-        if (n0 + r < a.n) store_values<JC, LPR>(a, n0 + r, mq + LPR * j0, v);
-      } else {
-#pragma unroll
-        for (int j = 0; j < JC; ++j) {
-          const bool ok = n0 + r < a.n && mq + LPR * (j0 + j) < a.m;
-          argmax_absorb<TS>(kb, ok ? argmax_key(v[j], (uint32_t)(n0 + r)) : 0ull, LPR * (j0 + j), lane);
-        }
-      }
+      xch_out<JC, LPR, TS>(a, n0, r, mq + LPR * j0, v, lane, kb);
     }
   }
 }
@@ -818,8 +888,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t*
       for (int j = 0; j < kGemvSteps; ++j) {
         const int gj = st.g + 4 * j;
         const uint32_t sb = (uint32_t)(gj >> 5) * kRecBytes;
-        st.v[j] = *reinterpret_cast<const uint4*>(tile_rec + (sb + (gj & 31) * 256 + voff));
-        if (!Q) st.b[j] = *reinterpret_cast<const uint2*>(tile_rec + (sb + (gj & 31) * 128 + boff));
+        st.v[j] = load_stream16(tile_rec + (sb + (gj & 31) * 256 + voff));
+        if (!Q) st.b[j] = load_stream8(tile_rec + (sb + (gj & 31) * 128 + boff));
       }
     };
     auto compute = [&](const GemvStage<M, Q>& st) {
@@ -904,8 +974,8 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
       const uint32_t o = j * blk_stride + rec_off;
-      st.v[j] = *reinterpret_cast<const uint4*>(blk + (o + (c & 7) * 1024 + lane * 16));
-      if (!Q) st.b[j] = *reinterpret_cast<const uint2*>(blk + (o + kViewBytes + (c & 7) * 512 + lane * 8));
+      st.v[j] = load_stream16(blk + (o + (c & 7) * 1024 + lane * 16));
+      if (!Q) st.b[j] = load_stream8(blk + (o + kViewBytes + (c & 7) * 512 + lane * 8));
     }
   };
   auto compute = [&](const MfmaStage<MT, RG, Q>& st) {

@@ -25,12 +25,29 @@ constexpr int kMaxGrid = 4096;                // most workgroups a GEMM launch u
 // split tile whose first unit it owns) plus the argmax completion counter.
 // Same size and place for every op and shape, and zero between calls.
 constexpr size_t kCounterBytes = W12_WS_COUNTER_BYTES;
+// Escape lines per matrix row (escapes x padded activation rows / N) above
+// which the MFMA kernel reads escape activations from a transposed copy of x.
+constexpr int64_t kXtEscRowLines = 16;
 static_assert(kCounterBytes >= (kMaxGrid + 1) * sizeof(uint32_t), "counter region too small");
 
 typedef short short2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Record loads: read once per GEMM, so marked non-temporal (streamed through
+// the caches with low retention; the activations, read by every workgroup,
+// stay cached instead).
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream8(const uint8_t* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
 
 // v_perm_b32 selectors over {S0 = view dword, S1 = B dword}: the result holds
 // two 16-bit halves [B byte | view byte] for weights (t, t+1) of the dword.
