@@ -290,6 +290,12 @@ struct HelperLds {
   int poff[64];              // exchange: slots of a chunk of participants
   uint32_t ready[2];  // streaming waves done with the partial buffer (cumulative)
   uint32_t consumed;  // segments whose partial sums the helper has taken
+  // The workgroup's final work, which all five waves share: published (fin = 1)
+  // by the helper once it knows it; kind 0: none, 1: the outputs of whole
+  // segment fin_si, 2: the sums of the split tiles this workgroup is last on.
+  uint32_t fin;
+  int fin_kind, fin_si, fin_n, fin_t[2], fin_pa[2], fin_pb[2];
+  uint32_t fin_last;
 };
 
 // Handshakes between the streaming waves and the helper through LDS counters
@@ -750,6 +756,79 @@ __device__ __forceinline__ void finish_argmax(const GemmParams& a, int p, int la
   }
 }
 
+// ------------------------------------------------------------ final work
+// The last piece of a workgroup's work comes after its stream, when the
+// streaming waves are idle: so all five waves share it, worker w taking
+// every fifth activation row (store mode; the argmax keys stay with the
+// helper, which holds them).
+constexpr int kWorkers = kStreamWaves + 1;
+
+// Split tile t, which this workgroup is last on: worker w's share of the sums
+// of all sharers' slots, added in workgroup order (the same order as the
+// helper alone would use).
+template <int MM, int TS>
+__device__ __forceinline__ void xch_sum_share(const GemmParams& a, int t, int pa, int pb, int lane, int w) {
+  constexpr int LPR = 64 / TS;
+  constexpr int MJ = (MM + LPR - 1) / LPR;
+  constexpr int J = (MJ + kWorkers - 1) / kWorkers;
+  constexpr int QX = 8;  // slots loaded per round trip
+  const int r = lane % TS, mq = lane / TS;
+  const int n0 = split_row0<TS / 16>(a, t);
+  float v[J];
+#pragma unroll
+  for (int i = 0; i < J; ++i) v[i] = 0.f;
+  bool started = false;  // adds start from the first slot (keeps the sign of a zero sum)
+  for (int q0 = pa; q0 <= pb; q0 += QX) {
+    const int nq = min(QX, pb - q0 + 1);
+    const int mine = lane < nq ? part_slot(a, q0 + lane, t) : -1;
+    float tv[QX][J];
+    bool has[QX];
+#pragma unroll
+    for (int u = 0; u < QX; ++u) {
+      const int sl = u < nq ? __builtin_amdgcn_readlane(mine, u) : -1;
+      has[u] = sl >= 0;
+      const int64_t base = (int64_t)max(sl, 0) * MM * TS;
+#pragma unroll
+      for (int i = 0; i < J; ++i) {
+        const int m = mq + LPR * (w + kWorkers * i);
+        tv[u][i] = (has[u] && m < a.m) ? load_shared(&a.part[base + m * TS + r]) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < QX; ++u) {
+      if (!has[u]) continue;
+#pragma unroll
+      for (int i = 0; i < J; ++i) v[i] = started ? v[i] + tv[u][i] : tv[u][i];
+      started = true;
+    }
+  }
+  if (n0 + r < a.n) store_values<J, LPR * kWorkers>(a, n0 + r, mq + LPR * w, v);
+}
+
+// Worker w's share of the final work the helper published.
+template <int MM, int ROWS, int TS>
+__device__ __forceinline__ void final_share(const GemmParams& a, const HelperLds<MM, ROWS>& h, const SegList& L,
+                                            int lane, int w) {
+  const int kind = __builtin_amdgcn_readfirstlane(h.fin_kind);
+  if (kind == 1) {
+    const int si = __builtin_amdgcn_readfirstlane(h.fin_si);
+    const Seg s = seg_at<ROWS / 16>(a, L, si);
+    constexpr int J = (MM + kWorkers - 1) / kWorkers;
+    const int r = lane < ROWS ? lane : ROWS - 1;
+    float v[J];
+    seg_values<J, kWorkers>(h, si % kSlots, r, w, v);
+    if (lane < s.rg * 16 && lane < ROWS) store_values<J, kWorkers>(a, s.row0 + lane, w, v);
+  } else if (kind == 2) {
+    const int nn = __builtin_amdgcn_readfirstlane(h.fin_n);
+    const uint32_t last = __builtin_amdgcn_readfirstlane(h.fin_last);
+    for (int c = 0; c < nn; ++c)
+      if ((last >> c) & 1u)
+        xch_sum_share<MM, TS>(a, __builtin_amdgcn_readfirstlane(h.fin_t[c]),
+                              __builtin_amdgcn_readfirstlane(h.fin_pa[c]),
+                              __builtin_amdgcn_readfirstlane(h.fin_pb[c]), lane, w);
+  }
+}
+
 // Correction target for segment j: its rows and columns.
 template <int GB>
 __device__ __forceinline__ Tgt seg_target(const GemmParams& a, const SegList& L, int j) {
@@ -806,9 +885,25 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
       compact(i & 1, i % kSlots, seg_at<GB>(a, L, i));
       lds_set(&h.consumed, (uint32_t)(i + 1));
     }
+    // the last group of a store-mode call is the shared final work
+    const bool shared = b1 == n && a.mode == kModeStore;
     Xch X{0, 0, 0, 0, 0, 0, 0, 0ull};
     if (split) X = xch_begin<MM, ROWS, TS>(a, h, L, p, b0, b1, lane);
-    else emit_whole<MM, ROWS>(a, h, L, b0, lane, kb);
+    else if (!shared) emit_whole<MM, ROWS>(a, h, L, b0, lane, kb);
+    if (shared) {
+      if (lane == 0) {
+        h.fin_kind = split ? 2 : 1;
+        h.fin_si = b0;
+        h.fin_n = X.n;
+        h.fin_t[0] = X.t0, h.fin_t[1] = X.t1;
+        h.fin_pa[0] = X.pa0, h.fin_pa[1] = X.pa1;
+        h.fin_pb[0] = X.pb0, h.fin_pb[1] = X.pb1;
+        h.fin_last = (uint32_t)X.last;
+      }
+      lds_set(&h.fin, 1u);
+      final_share<MM, ROWS, TS>(a, h, L, lane, kStreamWaves);
+      return;
+    }
     // segments before b1 are done with their slots: those of b1 .. b1 + 2 are
     // free (this also covers the next group)
     corr_upto(min(n, b1 + kSlots));
@@ -816,6 +911,9 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
     b0 = b1;
   }
   if (a.mode == kModeArgmax) finish_argmax(a, p, lane, kb);
+  // no shared final work (argmax mode, or no segments)
+  if (lane == 0) h.fin_kind = 0;
+  lds_set(&h.fin, 1u);
 }
 
 // ============================================================== GEMV (M < 16)
@@ -849,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t*
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x;
   const SegList L = seg_list<kGemvTileRows / 16>(a, p);
-  if (threadIdx.x == 0) sh.h.ready[0] = sh.h.ready[1] = sh.h.consumed = 0;
+  if (threadIdx.x == 0) sh.h.ready[0] = sh.h.ready[1] = sh.h.consumed = sh.h.fin = 0;
   __syncthreads();
   if (wave == kStreamWaves) {
     auto compact = [&](int buf, int sl, const Seg&) {
@@ -912,6 +1010,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t*
     for (int m = 0; m < M; ++m) sh.part[i & 1][wave][m][lane] = acc[m];
     if (lane == 0) lds_add(&sh.h.ready[i & 1]);
   }
+  // the workgroup's final work, shared with the helper
+  lds_wait_geq(&sh.h.fin, 1u);
+  final_share<M, kGemvTileRows, kGemvTileRows>(a, sh.h, L, lane, wave);
 }
 
 // ============================================================== MFMA (M >= 16)
@@ -1016,7 +1117,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x;
   const SegList L = seg_list<TB>(a, p);
-  if (threadIdx.x == 0) sh.h.ready[0] = sh.h.ready[1] = sh.h.consumed = 0;
+  if (threadIdx.x == 0) sh.h.ready[0] = sh.h.ready[1] = sh.h.consumed = sh.h.fin = 0;
   __syncthreads();
   if (wave == kStreamWaves) {
     // C of tile j at (row, m): lane (row/4)*16 + m%16, element row%4, m-tile m/16
@@ -1064,6 +1165,9 @@ __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
     }
     if (lane == 0) lds_add(&sh.h.ready[i & 1]);
   }
+  // the workgroup's final work, shared with the helper
+  lds_wait_geq(&sh.h.fin, 1u);
+  final_share<MT * 16, R * 16, TB * 16>(a, sh.h, L, lane, wave);
 }
 
 // ============================================================== activation transpose
