@@ -29,6 +29,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "W12 GEMM achieved HBM GB/s (% of peak) and µs/call at M=1 and M=32"
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "w12_gemm_mlp5120_pmc_traffic.md")
+GEMM_SOURCES = ["lossless_compressed_weight_amd/csrc/w12_gemm.hip", "lossless_compressed_weight_amd/csrc/w12_api.hip",
+                "lossless_compressed_weight_amd/csrc/w12_internal.h"]
 PEAK_GBS = 8000.0
 MS = (1, 32)
 
@@ -152,8 +155,11 @@ def main():
     algo_bytes = sum(pc["algo_bytes"] for pc in dom)
     dur_us = sum(pc["us_mean"] for pc in dom)
     achieved = algo_bytes / dur_us / 1e3
+    traffic = measured_traffic(dom_path)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_GBS, 4),
+                "traffic": traffic, "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+                "algo_bytes_per_call": round(algo_bytes / len(dom)),
                 "kernel": (f"w12_gemm {dom_path} path (M={dom[0]['m']}, gate/up/down), mean of per-call HIP events"
                            + (" (one call = k_xpose + k_mfma)" if dom_path == "mfma" else " (one call = k_gemv)"))}
 
@@ -173,6 +179,25 @@ def main():
            "pct_peak": round(100 * value / PEAK_GBS, 2),
            "per_call": per_call, "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(path):
+    """HBM bytes per call of `path` ("gemv" or "mfma") from the committed
+    rocprofv3 counter summary, or None when the GEMM sources have changed
+    since those counters were taken."""
+    import hashlib
+    try:
+        line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic_json: "))
+        rec = json.loads(line[len("traffic_json: "):])
+        h = hashlib.sha256()
+        for f in GEMM_SOURCES:
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["bytes_per_call"][path])
+    except (OSError, StopIteration, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(sub, encs, xs, rows, passes):
