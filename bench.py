@@ -142,7 +142,7 @@ def main():
                          "packed_gbs": round(packed / med / 1e3, 1),
                          "pct_peak_packed": round(100 * packed / med / 1e3 / PEAK_GBS, 2),
                          "algo_bytes": algo, "n_esc": mat.n_esc,
-                         "path": "gemv" if m < 2 else "mfma"})
+                         "path": "gemv" if m <= 2 else "mfma"})
         packed_step += packed
     value = packed_step / (ms_per_step * 1e-3) / 1e9
 

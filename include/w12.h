@@ -158,7 +158,7 @@ int w12_decode(const w12_matrix* m, uint16_t* w_out, void* stream);
  * x: BF16, row stride ldx >= K elements (a multiple of 8, at most 2^25),
  *    16-byte aligned rows.
  * y: BF16 or fp32 (y_dtype), row stride ldy >= N elements (below 2^31).
- * 1 <= M <= 64: M == 1 runs the wavefront GEMV kernel, M >= 2 the MFMA kernel
+ * 1 <= M <= 64: M <= 2 runs the wavefront GEMV kernel, M >= 3 the MFMA kernel
  * (M padded to a multiple of 16).
  * ws: w12_workspace_bytes(W12_OP_GEMM, n, k, M) bytes (device). */
 int w12_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,

@@ -1206,10 +1206,10 @@ hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, ui
 // ============================================================== planning
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t grid_override) {
   GemmPlan pl{};
-  // The GEMV kernel takes its activations as scalar operands; past one row
+  // The GEMV kernel takes its activations as scalar operands; past two rows
   // they no longer stay in the scalar cache, and the MFMA kernel (M padded to
-  // 16) is faster for every M from 2 up.
-  pl.mfma = (path == 2) || (path == 0 && m >= 2);
+  // 16) is faster from M = 3 up (measured over M = 1 .. 16).
+  pl.mfma = (path == 2) || (path == 0 && m >= 3);
   pl.ku = (int)(k / kUnitCols);
   const int64_t mt = (m + 15) / 16;
   pl.gb = pl.mfma ? (mt <= 2 ? kMfmaR<1> : kMfmaR<3>) : kGemvTileRows / 16;
