@@ -55,10 +55,11 @@ int check_gemm_args(const w12_matrix* m, const void* x, int64_t M, int64_t ldx, 
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// workspace: [counters | partial slots | argmax keys | transposed x], each
-// 256-byte aligned
+// workspace: [counters | partial slots | argmax keys | transposed x | x in
+// MFMA operand order], each 256-byte aligned
 size_t gemm_ws_bytes(const GemmPlan& pl) {
-  return round256(pl.ctr_bytes) + round256(pl.part_bytes) + round256(pl.key_bytes) + round256(pl.xt_bytes);
+  return round256(pl.ctr_bytes) + round256(pl.part_bytes) + round256(pl.key_bytes) + round256(pl.xt_bytes) +
+         round256(pl.xk_bytes);
 }
 
 GemmPlan make_plan(int64_t n, int64_t k, int64_t M, int op) {
@@ -101,14 +102,19 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   // transposed copy of x (one cache line per escape instead of one per
   // activation row), at the price of one more kernel; with few it gathers
   // them from x directly.
+  // The MFMA kernel also reads its B operands from a copy of x in operand
+  // order (fully coalesced loads); one kernel writes both copies.
   p.xt = nullptr;
-  const int64_t mm = ((M + 15) / 16) * 16;
-  if (pl.mfma && p.fix && pl.xt_bytes > 0 && m->n_esc * mm > kXtEscRowLines * m->n) {
-    uint16_t* xt = reinterpret_cast<uint16_t*>(wsb + round256(pl.ctr_bytes) + round256(pl.part_bytes) +
-                                               round256(pl.key_bytes));
-    const hipError_t ex = launch_xpose(x, ldx, (int)M, (int)(((M + 15) / 16) * 16), (int)m->k, xt, st);
+  p.xk = nullptr;
+  if (pl.mfma) {
+    const int64_t mm = ((M + 15) / 16) * 16;
+    char* xt_at = wsb + round256(pl.ctr_bytes) + round256(pl.part_bytes) + round256(pl.key_bytes);
+    uint16_t* xt = (p.fix && m->n_esc * mm > kXtEscRowLines * m->n) ? reinterpret_cast<uint16_t*>(xt_at) : nullptr;
+    uint16_t* xk = reinterpret_cast<uint16_t*>(xt_at + round256(pl.xt_bytes));
+    const hipError_t ex = launch_xpose(x, ldx, (int)M, (int)mm, (int)m->k, xt, xk, st);
     if (ex != hipSuccess) return hip_fail(ex, "activation transpose launch");
     p.xt = xt;
+    p.xk = xk;
   }
   int unsupported = 0;
   const hipError_t e = launch_gemm(pl, p, st, &unsupported);

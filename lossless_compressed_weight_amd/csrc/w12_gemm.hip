@@ -1050,26 +1050,19 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[j][mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const uint32_t c3800 = opaque_vgpr(0x38003800u);
-  // activation row mt*16 + lane%16, columns 16 (lane/16) + 0..15 of the chunk:
-  // per-lane byte offsets from the chunk. Past M the lane reads row 0: those
-  // B columns only feed output columns m >= M, which are never stored, so the
-  // loads need no predicate.
-  uint32_t xoff[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int row = mt * 16 + (lane & 15);
-    xoff[mt] = (uint32_t)((row < a.m ? row : 0) * a.ldx + (lane >> 4) * 16) * 2u;
-  }
+  // B operands from the copy of x in operand order: for chunk c, MFMA half h
+  // and m-tile mt, lane l's 8 activations (row mt*16 + l%16, columns
+  // 16 (l/16) + 8h + 0..7 of the chunk) are bytes 16 l of one contiguous
+  // kilobyte, so each load is fully coalesced.
+  const uint8_t* xk = reinterpret_cast<const uint8_t*>(a.xk) + lane * 16;
   const uint8_t* blk = a.rec + (int64_t)s * a.kb * kRecBytes;
   const uint32_t blk_stride = (uint32_t)(a.kb * kRecBytes);
   auto load = [&](MfmaStage<MT, RG, Q>& st, int kk) {
     const int c = kk * 4 + wave;
-    const char* xc = reinterpret_cast<const char*>(a.x + c * 64);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint4* xp = reinterpret_cast<const uint4*>(xc + xoff[mt]);
-      st.x[mt][0] = xp[0];
-      st.x[mt][1] = xp[1];
+      st.x[mt][0] = *reinterpret_cast<const uint4*>(xk + ((size_t)(2 * c) * MT + mt) * 1024);
+      st.x[mt][1] = *reinterpret_cast<const uint4*>(xk + ((size_t)(2 * c + 1) * MT + mt) * 1024);
     }
     const uint32_t rec_off = (uint32_t)(c >> 3) * kRecBytes;
 #pragma unroll
@@ -1171,10 +1164,11 @@ __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
 }
 
 // ============================================================== activation transpose
-// x [M, K] -> xt [K, MM]: 32 columns per workgroup through LDS, read in
-// 16-byte pieces along rows of x and written in 16-byte pieces along rows of xt.
+// x [M, K] -> xt [K, MM] and xk (the MFMA kernel's B operand order): 32
+// columns per workgroup through LDS, read in 16-byte pieces along rows of x and
+// written in 16-byte pieces.
 __global__ __launch_bounds__(256) void k_xpose(const uint16_t* __restrict__ x, int64_t ldx, int M, int MM,
-                                               uint16_t* __restrict__ xt) {
+                                               uint16_t* __restrict__ xt, uint16_t* __restrict__ xk) {
   __shared__ uint16_t t[64][32 + 8];  // [m][column], rows padded to keep 16-byte alignment
   const int c0 = blockIdx.x * 32;
   // MM rows x 4 pieces of 8 columns
@@ -1185,21 +1179,34 @@ __global__ __launch_bounds__(256) void k_xpose(const uint16_t* __restrict__ x, i
     *reinterpret_cast<uint4*>(&t[m][8 * q]) = v;
   }
   __syncthreads();
-  // 32 columns x MM / 8 pieces of 8 activation rows
+  // xt: 32 columns x MM / 8 pieces of 8 activation rows
   const int pr = MM / 8;
-  for (int i = threadIdx.x; i < 32 * pr; i += 256) {
-    const int c = i / pr, q = i - c * pr;
-    uint32_t w[4];
+  if (xt) {
+    for (int i = threadIdx.x; i < 32 * pr; i += 256) {
+      const int c = i / pr, q = i - c * pr;
+      uint32_t w[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = (uint32_t)t[8 * q + 2 * j][c] | (uint32_t)t[8 * q + 2 * j + 1][c] << 16;
-    *reinterpret_cast<uint4*>(xt + (int64_t)(c0 + c) * MM + 8 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)t[8 * q + 2 * j][c] | (uint32_t)t[8 * q + 2 * j + 1][c] << 16;
+      *reinterpret_cast<uint4*>(xt + (int64_t)(c0 + c) * MM + 8 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  // xk: MM rows x 4 pieces of 8 columns, each to its operand slot
+  if (xk) {
+    const int MT = MM / 16;
+    for (int i = threadIdx.x; i < MM * 4; i += 256) {
+      const int m = i >> 2, col = c0 + 8 * (i & 3);
+      const int ch = col >> 6, w = col & 63, q = w >> 4, h = (w >> 3) & 1;
+      const int64_t o = ((((int64_t)(2 * ch + h) * MT + (m >> 4)) * 4 + q) * 16 + (m & 15)) * 8;
+      *reinterpret_cast<uint4*>(xk + o) = *reinterpret_cast<const uint4*>(&t[m][8 * (i & 3)]);
+    }
   }
 }
 
-hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, uint16_t* xt, hipStream_t s) {
-  if (mm > 64 || mm % 16 != 0 || M > mm || K % 32 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_xpose, dim3(K / 32), dim3(256), 0, s, x, ldx, M, mm, xt);
+hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, uint16_t* xt, uint16_t* xk,
+                        hipStream_t s) {
+  if (mm > 64 || mm % 16 != 0 || M > mm || K % 64 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_xpose, dim3(K / 32), dim3(256), 0, s, x, ldx, M, mm, xt, xk);
   return hipGetLastError();
 }
 
@@ -1239,6 +1246,7 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t gr
   pl.part_bytes = (size_t)(2 * P) * (size_t)mm * pl.tile_rows * sizeof(float);
   pl.key_bytes = (op == W12_OP_LMHEAD_ARGMAX) ? (size_t)P * (size_t)m * 8 : 0;
   pl.xt_bytes = pl.mfma ? (size_t)k * (size_t)mm * sizeof(uint16_t) : 0;
+  pl.xk_bytes = pl.xt_bytes;
   return pl;
 }
 

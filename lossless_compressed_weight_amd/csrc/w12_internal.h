@@ -153,6 +153,8 @@ struct GemmParams {
   const uint16_t* x;
   int64_t ldx;
   const uint16_t* xt;        // x transposed, [K][16 * ceil(M / 16)], rows past M zero (or null)
+  const uint16_t* xk;        // x in MFMA operand order (MFMA kernel), rows past M zero:
+                             // [K / 64][2][MT][4][16][8], one kilobyte per chunk, half and m-tile
   void* y;
   int64_t ldy;
   uint32_t* ctr;             // split-tile counters [tiles], then the argmax counter; zero between calls
@@ -199,10 +201,13 @@ struct GemmPlan {
   size_t part_bytes;
   size_t key_bytes;
   size_t xt_bytes;
+  size_t xk_bytes;
 };
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t grid_override);
 hipError_t launch_gemm(const GemmPlan& plan, GemmParams p, hipStream_t s, int* unsupported);
-// x [M, K] (row stride ldx) -> xt [K, mm] (mm = 16 * ceil(M / 16)), rows past M zero.
-hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, uint16_t* xt, hipStream_t s);
+// x [M, K] (row stride ldx) -> xt [K, mm] (mm = 16 * ceil(M / 16)) and xk (MFMA operand order), rows
+// past M zero; either output may be null.
+hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, uint16_t* xt, uint16_t* xk,
+                        hipStream_t s);
 
 }  // namespace w12
