@@ -291,11 +291,10 @@ struct HelperLds {
   uint32_t ready[2];  // streaming waves done with the partial buffer (cumulative)
   uint32_t consumed;  // segments whose partial sums the helper has taken
   // The workgroup's final work, which all five waves share: published (fin = 1)
-  // by the helper once it knows it; kind 0: none, 1: the outputs of whole
-  // segment fin_si, 2: the sums of the split tiles this workgroup is last on.
+  // by the helper once it knows it: the outputs of whole segment fin_si (if
+  // not -1), and the sums of the fin_n split tiles this workgroup is last on.
   uint32_t fin;
-  int fin_kind, fin_si, fin_n, fin_t[2], fin_pa[2], fin_pb[2];
-  uint32_t fin_last;
+  int fin_si, fin_n, fin_t[2], fin_pa[2], fin_pb[2];
 };
 
 // Handshakes between the streaming waves and the helper through LDS counters
@@ -809,24 +808,19 @@ __device__ __forceinline__ void xch_sum_share(const GemmParams& a, int t, int pa
 template <int MM, int ROWS, int TS>
 __device__ __forceinline__ void final_share(const GemmParams& a, const HelperLds<MM, ROWS>& h, const SegList& L,
                                             int lane, int w) {
-  const int kind = __builtin_amdgcn_readfirstlane(h.fin_kind);
-  if (kind == 1) {
-    const int si = __builtin_amdgcn_readfirstlane(h.fin_si);
+  const int si = __builtin_amdgcn_readfirstlane(h.fin_si);
+  if (si >= 0) {
     const Seg s = seg_at<ROWS / 16>(a, L, si);
     constexpr int J = (MM + kWorkers - 1) / kWorkers;
     const int r = lane < ROWS ? lane : ROWS - 1;
     float v[J];
     seg_values<J, kWorkers>(h, si % kSlots, r, w, v);
     if (lane < s.rg * 16 && lane < ROWS) store_values<J, kWorkers>(a, s.row0 + lane, w, v);
-  } else if (kind == 2) {
-    const int nn = __builtin_amdgcn_readfirstlane(h.fin_n);
-    const uint32_t last = __builtin_amdgcn_readfirstlane(h.fin_last);
-    for (int c = 0; c < nn; ++c)
-      if ((last >> c) & 1u)
-        xch_sum_share<MM, TS>(a, __builtin_amdgcn_readfirstlane(h.fin_t[c]),
-                              __builtin_amdgcn_readfirstlane(h.fin_pa[c]),
-                              __builtin_amdgcn_readfirstlane(h.fin_pb[c]), lane, w);
   }
+  const int nn = __builtin_amdgcn_readfirstlane(h.fin_n);
+  for (int c = 0; c < nn; ++c)
+    xch_sum_share<MM, TS>(a, __builtin_amdgcn_readfirstlane(h.fin_t[c]), __builtin_amdgcn_readfirstlane(h.fin_pa[c]),
+                          __builtin_amdgcn_readfirstlane(h.fin_pb[c]), lane, w);
 }
 
 // Correction target for segment j: its rows and columns.
@@ -877,6 +871,19 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
   // the first three segments' corrections in one pass (the round trips cost
   // the same for one target as for three)
   corr_upto(min(n, kSlots));
+  // Store mode: the sums of the split tiles this workgroup is last on wait for
+  // the shared final work (a workgroup has at most two split tiles).
+  const bool store = a.mode == kModeStore;
+  int npend = 0, pt0 = 0, pa0 = 0, pb0 = 0, pt1 = 0, pa1 = 0, pb1 = 0;
+  auto publish = [&](int si) {
+    if (lane == 0) {
+      h.fin_si = si;
+      h.fin_n = npend;
+      h.fin_t[0] = pt0, h.fin_pa[0] = pa0, h.fin_pb[0] = pb0;
+      h.fin_t[1] = pt1, h.fin_pa[1] = pa1, h.fin_pb[1] = pb1;
+    }
+    lds_set(&h.fin, 1u);
+  };
   for (int b0 = 0; b0 < n;) {
     const bool split = b0 < L.nsk;
     const int b1 = group_end(b0);  // (their corrections were gathered ahead)
@@ -885,35 +892,36 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
       compact(i & 1, i % kSlots, seg_at<GB>(a, L, i));
       lds_set(&h.consumed, (uint32_t)(i + 1));
     }
-    // the last group of a store-mode call is the shared final work
-    const bool shared = b1 == n && a.mode == kModeStore;
+    // the last group of a store-mode call is part of the shared final work
+    const bool shared = b1 == n && store;
     Xch X{0, 0, 0, 0, 0, 0, 0, 0ull};
     if (split) X = xch_begin<MM, ROWS, TS>(a, h, L, p, b0, b1, lane);
     else if (!shared) emit_whole<MM, ROWS>(a, h, L, b0, lane, kb);
-    if (shared) {
-      if (lane == 0) {
-        h.fin_kind = split ? 2 : 1;
-        h.fin_si = b0;
-        h.fin_n = X.n;
-        h.fin_t[0] = X.t0, h.fin_t[1] = X.t1;
-        h.fin_pa[0] = X.pa0, h.fin_pa[1] = X.pa1;
-        h.fin_pb[0] = X.pb0, h.fin_pb[1] = X.pb1;
-        h.fin_last = (uint32_t)X.last;
+    if (store && split) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (c < X.n && ((X.last >> c) & 1)) {
+          const int t = c == 0 ? X.t0 : X.t1, qa = c == 0 ? X.pa0 : X.pa1, qb = c == 0 ? X.pb0 : X.pb1;
+          if (npend == 0) pt0 = t, pa0 = qa, pb0 = qb;
+          else pt1 = t, pa1 = qa, pb1 = qb;
+          ++npend;
+        }
       }
-      lds_set(&h.fin, 1u);
+    }
+    if (shared) {
+      publish(split ? -1 : b0);
       final_share<MM, ROWS, TS>(a, h, L, lane, kStreamWaves);
       return;
     }
     // segments before b1 are done with their slots: those of b1 .. b1 + 2 are
     // free (this also covers the next group)
     corr_upto(min(n, b1 + kSlots));
-    if (split) xch_end<MM, ROWS, TS>(a, h, X, lane, kb);
+    if (split && !store) xch_end<MM, ROWS, TS>(a, h, X, lane, kb);
     b0 = b1;
   }
   if (a.mode == kModeArgmax) finish_argmax(a, p, lane, kb);
-  // no shared final work (argmax mode, or no segments)
-  if (lane == 0) h.fin_kind = 0;
-  lds_set(&h.fin, 1u);
+  // no segments, or argmax mode: nothing (else) to share
+  publish(-1);
 }
 
 // ============================================================== GEMV (M < 16)
