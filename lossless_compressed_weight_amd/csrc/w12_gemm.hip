@@ -871,9 +871,13 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
   // the first three segments' corrections in one pass (the round trips cost
   // the same for one target as for three)
   corr_upto(min(n, kSlots));
-  // Store mode: the sums of the split tiles this workgroup is last on wait for
-  // the shared final work (a workgroup has at most two split tiles).
+  // Store mode, when a split tile's sum is a long job (more than 8 values per
+  // lane): the sums of the split tiles this workgroup is last on wait for the
+  // shared final work (a workgroup has at most two split tiles). Short sums
+  // are done at once, hidden behind the stream.
   const bool store = a.mode == kModeStore;
+  constexpr bool kDefer = (MM + 64 / TS - 1) / (64 / TS) > 8;
+  const bool defer = store && kDefer;
   int npend = 0, pt0 = 0, pa0 = 0, pb0 = 0, pt1 = 0, pa1 = 0, pb1 = 0;
   auto publish = [&](int si) {
     if (lane == 0) {
@@ -897,7 +901,7 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
     Xch X{0, 0, 0, 0, 0, 0, 0, 0ull};
     if (split) X = xch_begin<MM, ROWS, TS>(a, h, L, p, b0, b1, lane);
     else if (!shared) emit_whole<MM, ROWS>(a, h, L, b0, lane, kb);
-    if (store && split) {
+    if ((defer || shared) && split) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         if (c < X.n && ((X.last >> c) & 1)) {
@@ -916,7 +920,7 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
     // segments before b1 are done with their slots: those of b1 .. b1 + 2 are
     // free (this also covers the next group)
     corr_upto(min(n, b1 + kSlots));
-    if (split && !store) xch_end<MM, ROWS, TS>(a, h, X, lane, kb);
+    if (split && !defer) xch_end<MM, ROWS, TS>(a, h, X, lane, kb);
     b0 = b1;
   }
   if (a.mode == kModeArgmax) finish_argmax(a, p, lane, kb);
