@@ -531,15 +531,68 @@ __device__ __forceinline__ void seg_values(const HelperLds<MM, ROWS>& h, int sl,
   for (int j = 0; j < J; ++j) v[j] = (c[j] * s - cn[j]) + cp[j];
 }
 
+// The largest key over all 64 lanes (every lane must be active).
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long key) {
+  key = max_u64(key, row_ror_u64<0x121>(key));
+  key = max_u64(key, row_ror_u64<0x122>(key));
+  key = max_u64(key, row_ror_u64<0x124>(key));
+  key = max_u64(key, row_ror_u64<0x128>(key));
+  return max_u64(max_u64(readlane_u64(key, 0), readlane_u64(key, 16)),
+                 max_u64(readlane_u64(key, 32), readlane_u64(key, 48)));
+}
+
+// One activation row m of a 64-row tile (lane = row n0 + lane): fold the
+// tile's best key into lane m's kb. The value half of the keys is reduced
+// first (DPP row maxima, then the four rows); the lowest valid lane holding
+// it gives the index half, so ties go to the lowest row. All lanes active.
+__device__ __forceinline__ uint32_t row_ror_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x121, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x122, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));
+  return v;
+}
+
+__device__ __forceinline__ void argmax_tile64(unsigned long long& kb, float v, bool valid, int n0, int m, int lane) {
+  const uint32_t hi = valid ? (uint32_t)(argmax_key(v, 0u) >> 32) : 0u;
+  const uint32_t rm = row_ror_max_u32(hi);
+  const uint32_t mx = max(max((uint32_t)__builtin_amdgcn_readlane((int)rm, 0), (uint32_t)__builtin_amdgcn_readlane((int)rm, 16)),
+                          max((uint32_t)__builtin_amdgcn_readlane((int)rm, 32), (uint32_t)__builtin_amdgcn_readlane((int)rm, 48)));
+  const uint64_t cand = __ballot(valid && hi == mx);
+  if (cand != 0 && lane == m) {
+    const uint32_t n = (uint32_t)(n0 + __builtin_ctzll(cand));
+    kb = max_u64(kb, (unsigned long long)mx << 32 | (0xFFFFFFFFu - n));
+  }
+}
+
+// Argmax of whole tiles: each lane keeps the best
+// key of its own rows per activation row (lb), folded into kb once at the end
+// (up to 16 activation rows: beyond that the registers run out).
+constexpr int kLaneBestRows = 16;
+
 // Whole-tile segment si (slot si % 3), lane = row: its outputs or argmax keys.
 template <int MM, int ROWS>
 __device__ __forceinline__ void emit_whole(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int si,
-                                           int lane, unsigned long long& kb) {
+                                           int lane, unsigned long long& kb,
+                                           unsigned long long (&lb)[MM <= kLaneBestRows ? MM : 1]) {
   const Seg s = seg_at<ROWS / 16>(a, L, si);
   const int sl = si % kSlots, n0 = s.row0;
   const bool valid = lane < s.rg * 16 && lane < ROWS;
   const int r = lane < ROWS ? lane : ROWS - 1;
   constexpr int C = MM < 16 ? MM : 16;
+  if constexpr (MM <= kLaneBestRows) {
+    if (a.mode == kModeArgmax) {
+#pragma unroll
+      for (int m0 = 0; m0 < MM; m0 += C) {
+        float v[C];
+        seg_values<C, 1>(h, sl, r, m0, v);
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+          lb[m0 + j] = max_u64(lb[m0 + j], valid ? argmax_key(v[j], (uint32_t)(n0 + lane)) : 0ull);
+      }
+      return;
+    }
+  }
 #pragma unroll 1
   for (int m0 = 0; m0 < MM; m0 += C) {
     if (m0 < a.m) {
@@ -550,8 +603,7 @@ __device__ __forceinline__ void emit_whole(const GemmParams& a, HelperLds<MM, RO
       } else {
 #pragma unroll
         for (int j = 0; j < C; ++j)
-          if (m0 + j < a.m)
-            argmax_absorb<64>(kb, valid ? argmax_key(v[j], (uint32_t)(n0 + lane)) : 0ull, m0 + j, lane);
+          if (m0 + j < a.m) argmax_tile64(kb, v[j], valid, n0, m0 + j, lane);
       }
     }
   }
@@ -735,7 +787,8 @@ __device__ __forceinline__ void xch_end(const GemmParams& a, HelperLds<MM, ROWS>
 }
 
 // Argmax mode: publish this workgroup's best key per activation row; the last
-// workgroup to finish reduces all of them into idx / max.
+// workgroup to finish reduces all of them into idx / max, lane = workgroup
+// (64 at a time) and 8 activation rows per round trip.
 __device__ __forceinline__ void finish_argmax(const GemmParams& a, int p, int lane, unsigned long long kb) {
   if (lane < a.m) store_shared(&a.keys[(int64_t)p * a.m + lane], kb);
   __builtin_amdgcn_s_waitcnt(0);
@@ -744,14 +797,33 @@ __device__ __forceinline__ void finish_argmax(const GemmParams& a, int p, int la
     last = __builtin_amdgcn_atomic_inc32(&a.ctr[kMaxGrid], (uint32_t)a.P - 1, __ATOMIC_RELAXED, "agent") ==
            (uint32_t)a.P - 1;
   if (__ballot(last) == 0) return;
-  if (lane < a.m) {
-    unsigned long long best = 0ull;
-    for (int q = 0; q < a.P; ++q) {
-      const unsigned long long k = load_shared(&a.keys[(int64_t)q * a.m + lane]);
-      best = k > best ? k : best;
+  constexpr int MC = 8, QB = 4;
+  for (int m0 = 0; m0 < a.m; m0 += MC) {
+    unsigned long long best[MC];
+#pragma unroll
+    for (int j = 0; j < MC; ++j) best[j] = 0ull;
+    for (int q0 = 0; q0 < a.P; q0 += 64 * QB) {
+      unsigned long long k[MC][QB];
+#pragma unroll
+      for (int j = 0; j < MC; ++j)
+#pragma unroll
+        for (int i = 0; i < QB; ++i) {
+          const int q = q0 + 64 * i + lane, m = m0 + j;
+          k[j][i] = (q < a.P && m < a.m) ? load_shared(&a.keys[(int64_t)q * a.m + m]) : 0ull;
+        }
+#pragma unroll
+      for (int j = 0; j < MC; ++j)
+#pragma unroll
+        for (int i = 0; i < QB; ++i) best[j] = max_u64(best[j], k[j][i]);
     }
-    a.idx[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
-    if (a.maxv) a.maxv[lane] = key_value(best);
+#pragma unroll
+    for (int j = 0; j < MC; ++j) {
+      const unsigned long long b = wave_max_u64(best[j]);
+      if (lane == 0 && m0 + j < a.m) {
+        a.idx[m0 + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
+        if (a.maxv) a.maxv[m0 + j] = key_value(b);
+      }
+    }
   }
 }
 
@@ -847,6 +919,9 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
   __builtin_amdgcn_s_setprio(3);
   constexpr int GB = ROWS / 16;  // 16-row blocks of a whole tile
   unsigned long long kb = 0ull;  // argmax: lane m's best key of activation row m
+  unsigned long long lb[MM <= kLaneBestRows ? MM : 1];  // argmax: this lane's rows' best key per activation row
+#pragma unroll
+  for (int m = 0; m < (MM <= kLaneBestRows ? MM : 1); ++m) lb[m] = 0ull;
   const int n = L.n;
   const Tgt z{0, 0, 0, 0, 0};
   int corr_end = 0;  // segments [0, corr_end) have their corrections
@@ -900,7 +975,7 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
     const bool shared = b1 == n && store;
     Xch X{0, 0, 0, 0, 0, 0, 0, 0ull};
     if (split) X = xch_begin<MM, ROWS, TS>(a, h, L, p, b0, b1, lane);
-    else if (!shared) emit_whole<MM, ROWS>(a, h, L, b0, lane, kb);
+    else if (!shared) emit_whole<MM, ROWS>(a, h, L, b0, lane, kb, lb);
     if ((defer || shared) && split) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -923,7 +998,14 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
     if (split && !defer) xch_end<MM, ROWS, TS>(a, h, X, lane, kb);
     b0 = b1;
   }
-  if (a.mode == kModeArgmax) finish_argmax(a, p, lane, kb);
+  if (a.mode == kModeArgmax) {
+    if constexpr (MM <= kLaneBestRows) {
+#pragma unroll
+      for (int m = 0; m < MM; ++m)
+        if (m < a.m) argmax_absorb<64>(kb, lb[m], m, lane);
+    }
+    finish_argmax(a, p, lane, kb);
+  }
   // no segments, or argmax mode: nothing (else) to share
   publish(-1);
 }
