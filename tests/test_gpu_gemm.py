@@ -230,6 +230,38 @@ def test_lmhead_argmax_small(m):
     del rng
 
 
+@pytest.mark.parametrize("m", [1, 2, 3, 16, 17, 33, 48, 64])
+def test_lmhead_argmax_whole_tiles(m):
+    """Enough rows that every workgroup also owns whole tiles (the per-lane and
+    per-tile argmax folds), with exact ties planted in different whole tiles:
+    the lowest row must win."""
+    n, k = 20480, 1024
+    w = synth.workload_matrix(3, 0, rows=slice(0, n))[:, :k].copy()
+    x = synth.make_activations(m, k, seed=900 + m)
+    # row 9000 scaled by 2^14 (exponent field + 14, exact) leads for many
+    # activation rows; rows 3000 and 15000 (other whole tiles and workgroups,
+    # which add up K in the same order) copy it
+    e = (w[9000] >> 7) & 0xFF
+    w[9000] = np.where((e > 0) & (e < 240), w[9000] + (14 << 7), w[9000]).astype(np.uint16)
+    w[3000] = w[9000]
+    w[15000] = w[9000]
+    log(f"[argmax whole tiles] {n}x{k} M={m}")
+    mat = w12.encode(dev16(w))
+    idx, mx = w12.lmhead_argmax(mat, dev16(x))
+    yf = w12.gemm(mat, dev16(x), torch.float32).cpu().numpy()
+    idx = idx.cpu().numpy().astype(np.int64)
+    assert np.array_equal(idx, np.argmax(yf, axis=1))
+    assert np.array_equal(mx.cpu().numpy().view(np.uint32), yf[np.arange(m), idx].view(np.uint32))
+    y64 = o.gemm_ref(x, w)
+    ridx, margin = o.argmax_ref(y64)
+    far = margin >= 1e-3
+    assert np.array_equal(idx[far], ridx[far])
+    # where the planted rows lead, the lowest of the three wins
+    lead = np.isin(ridx, [3000, 9000, 15000])
+    assert lead.sum() >= 1 if m > 2 else True
+    assert np.all(idx[lead] == 3000)
+
+
 def test_lmhead_argmax_planted_ties_and_negatives():
     """All-negative logits, exact ties (lowest index wins) and -0 vs +0."""
     k = 512
