@@ -22,7 +22,8 @@
 // dependent round trips: it adds the partial sums, gathers the per-row scales
 // and escape corrections, and finishes segments - whole tiles by storing
 // them, split tiles by the exchange below. A workgroup streams its (short)
-// split segments first, so their exchange overlaps its whole tiles.
+// split segments first, so their exchange overlaps its whole tiles. The last
+// piece of its work, after the stream, is shared by all five waves.
 //
 // Segment value, per output row and activation row: A = sum of x * w' over the
 // segment's columns, where w' is the weight decoded with a fixed exponent
@@ -274,9 +275,8 @@ __device__ __forceinline__ void pipeline(int u, int ue, Load&& load, Compute&& c
 
 // ============================================================== helper wave
 // Per-segment state the helper keeps in LDS, in slot (segment index % 3):
-// the segment's values [m][row] (first the plain sums A, then the finished
-// values), its corrections CN and CP, and its rows' scales; plus the work
-// list of the corrections.
+// the segment's plain sums A [m][row], its corrections CN and CP, and its
+// rows' scales; plus the work list of the corrections.
 template <int MM, int ROWS>
 struct HelperLds {
   float cv[kSlots][MM][ROWS];
@@ -300,8 +300,9 @@ struct HelperLds {
 // Handshakes between the streaming waves and the helper through LDS counters
 // (no barrier, so neither side waits for the other's memory round trips).
 // Every wait ends: the helper waits only for counters the streaming waves
-// raise after each segment, and a streaming wave only for the helper to take
-// the segment two back, which needs nothing from that wave.
+// raise after each segment; a streaming wave waits only for the helper to take
+// the segment two back, which needs nothing from that wave, and at the end for
+// the helper's notice of the final work, which every path of the helper posts.
 __device__ __forceinline__ void lds_wait_geq(const uint32_t* c, uint32_t v) {
   while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < v) __builtin_amdgcn_s_sleep(1);
 }
@@ -565,9 +566,9 @@ __device__ __forceinline__ void argmax_tile64(unsigned long long& kb, float v, b
   }
 }
 
-// Argmax of whole tiles: each lane keeps the best
-// key of its own rows per activation row (lb), folded into kb once at the end
-// (up to 16 activation rows: beyond that the registers run out).
+// Argmax of whole tiles: each lane keeps the best key of its own rows per
+// activation row (lb), folded into kb once at the end (up to 16 activation
+// rows; beyond that the registers run out and each tile is folded at once).
 constexpr int kLaneBestRows = 16;
 
 // Whole-tile segment si (slot si % 3), lane = row: its outputs or argmax keys.
