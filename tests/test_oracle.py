@@ -131,6 +131,12 @@ def test_window_all_escape_row_and_ties():
     # 256 weights at exponent 100 and 256 at 116: tops 100..115 hold 256, 116 holds 256 too
     row = np.array([[100 << 7] * 256 + [116 << 7] * 256], dtype=np.uint16)
     assert o.window_tops(row)[0] == 116
+    # a narrow cluster (exponents 100..103): every top from 103 to 115 covers all
+    # of it, and the tie goes to the largest normal exponent, 103; inf, NaN, zero
+    # and subnormal weights in the row do not move that cap
+    base = [(100 + i % 4) << 7 | (i % 128) for i in range(508)]
+    row = np.array([base + [0x7F80, 0xFFC0, 0x0000, 0x0005]], dtype=np.uint16)
+    assert o.window_tops(row)[0] == 103
 
 
 # --- escapes and fields --------------------------------------------------------------
@@ -334,6 +340,41 @@ def test_q_view_closed_form():
     ok = ~esc
     ulp4 = 2.0 ** ((v // 8) % 16 + E - 15 - 127 - 3)
     assert np.all(np.abs(q - x)[ok] <= (ulp4 / 2)[ok])
+
+
+def test_gemm_q8_ref_brute_force():
+    """The Q pass product on a tiny matrix with escapes: an exact rational sum
+    over weights written from the view bytes by the midpoint rule, with each
+    escape's placeholder in place of its value (section 4.3, zero-copy Q pass).
+    """
+    w = _mixed_matrix()[:16].copy()
+    w[:, 40:] = synth.workload_matrix(0, 0)[:16, 40:512]
+    enc = o.encode(w)
+    assert enc.n_esc > 0
+    view, _ = o.unpack_records(enc.records, enc.n, enc.k)
+    cols = 48
+    x = synth.make_activations(2, 512, seed=14)
+    x[:, cols:] = 0
+    xv = o.bf16_to_f64(x)
+    want = [[Fraction(0)] * 16 for _ in range(2)]
+    bound = np.zeros((2, 16))
+    for n in range(16):
+        E = int(enc.e_top[n])
+        for c in range(cols):
+            v = int(view[n, c])
+            q = Fraction(-1 if v >= 128 else 1) * Fraction(2) ** ((v >> 3) % 16 + E - 15 - 127) * \
+                (1 + Fraction(v % 8, 8) + Fraction(8, 128))
+            for i in range(2):
+                want[i][n] += Fraction(float(xv[i, c])) * q
+                bound[i, n] += abs(float(xv[i, c]) * float(q))
+    got = o.gemm_q8_ref(x, enc)
+    for i in range(2):
+        for n in range(16):
+            err = abs(Fraction(float(got[i, n])) - want[i][n])
+            assert err <= Fraction(cols * 2.0 ** -53 * bound[i, n]), (i, n)
+    # the placeholders, not the escapes' own values, enter the Q product
+    hit = enc.esc["col"] < cols
+    assert np.any(enc.esc["bits"][hit] != enc.esc["ph"][hit])
 
 
 def test_argmax_planted_winners():
