@@ -189,8 +189,9 @@ int w12_validate(const w12_matrix* m, void* ws, size_t ws_bytes, void* stream);
 /* Test and tuning hooks (process-wide, not thread-safe; call before launching).
  * W12_TUNE_PATH: 0 = choose by M, 1 = force the GEMV kernel (M <= 16),
  *   2 = force the MFMA kernel.
- * W12_TUNE_GRID: workgroup count for the GEMM kernels (0 = default; at most
- *   4096 and at most the number of work units are used).
+ * W12_TUNE_GRID: workgroup count for the GEMM kernels (0 = the library's
+ *   choice: 256, or c * T for a matrix of T < 256 tiles; at most 4096 and at
+ *   most the number of work units are used).
  * Changing W12_TUNE_GRID changes the fp32 summation order and the workspace
  * size; query w12_workspace_bytes after setting it. Returns the old value. */
 #define W12_TUNE_PATH 1

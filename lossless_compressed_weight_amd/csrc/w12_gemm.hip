@@ -1320,7 +1320,24 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t gr
   // One workgroup per compute unit: its four streaming waves keep enough
   // loads in flight, and the whole tiles go round-robin over the CUs.
   int64_t P = kNumCU;
-  if (grid_override > 0) P = grid_override;
+  if (grid_override > 0) {
+    P = grid_override;
+  } else if (tiles < kNumCU) {
+    // Fewer tiles than CUs: every tile is split. Splitting each tile into the
+    // same number c of parts (c * tiles workgroups) beats spreading the units
+    // over all CUs, where tiles have unequal parts and workgroups two of them
+    // (measured on 6144 x 5120, 5120 x 6144 and 5120 x 17408 at M = 1 .. 64).
+    const int64_t c = kNumCU / tiles;
+    if (c >= 2) {
+      P = c * tiles;
+    } else {
+      // One part per tile (whole tiles, no exchange) leaves kNumCU - tiles
+      // CUs idle: worth it while the extra bytes per workgroup stay small
+      // against what the exchange of split tiles costs.
+      const int64_t tile_bytes = pl.gb * 16 * k * 3 / 2;
+      if (tile_bytes * (kNumCU - tiles) <= kWholeTileSlack * kNumCU) P = tiles;
+    }
+  }
   if (P > kMaxGrid) P = kMaxGrid;
   if (P > tiles * pl.ku) P = tiles * pl.ku;
   if (P < 1) P = 1;

@@ -21,6 +21,7 @@ constexpr int kRecBytes = W12_REC_BYTES;      // 12288
 constexpr int kViewBytes = W12_REC_VIEW_BYTES;  // 8192
 constexpr int kNumCU = 256;                   // MI355X compute units (sizes the stream-K grid)
 constexpr int kMaxGrid = 4096;                // most workgroups a GEMM launch uses
+constexpr int64_t kWholeTileSlack = 192 << 10;  // extra bytes per workgroup whole tiles may cost (see plan_gemm)
 // Counter words at the start of every GEMM workspace: one per workgroup (the
 // split tile whose first unit it owns) plus the argmax completion counter.
 // Same size and place for every op and shape, and zero between calls.

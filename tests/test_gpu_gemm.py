@@ -80,6 +80,26 @@ def test_split_reduction_any_grid(grid, m, path):
     check_f32(yf, o.gemm_ref(x, w), f"grid={grid} M={m} path={path}")
 
 
+@pytest.mark.parametrize("n,k,m", [
+    (6144, 512, 1), (6144, 512, 32),   # 96 tiles: two equal sharers per tile (192 workgroups)
+    (5120, 512, 2), (5120, 512, 20),   # 80 tiles, two units each: capped at 160 workgroups
+    (5120, 1024, 48), (5120, 1024, 64),  # 160 tiles of 32 rows: whole tiles, no exchange
+    (4096, 1024, 16),                  # 64 tiles: four sharers per tile
+])
+def test_default_grid_for_fewer_tiles_than_cus(n, k, m):
+    """With fewer tiles than compute units the library picks the grid by the
+    tile count (equal sharers per tile, or whole tiles on fewer workgroups):
+    each such plan matches the oracle."""
+    w = synth.make_weights(n, k, synth.WORKLOADS[0], seed=n + k)
+    log(f"[default grid] {n}x{k} M={m}")
+    x = synth.make_activations(m, k, seed=31 + m)
+    mat = w12.encode(dev16(w))
+    yf, yb = gemm_both(mat, dev16(x))
+    y64 = o.gemm_ref(x, w)
+    check_f32(yf, y64, f"{n}x{k} M={m}")
+    check_bf16(yb, yf, y64, f"{n}x{k} M={m}")
+
+
 def test_gemv_and_mfma_paths_agree_at_m16():
     w = synth.workload_matrix(0, 0)
     x = synth.make_activations(16, 1024, seed=99)
