@@ -274,6 +274,18 @@ __device__ __forceinline__ void pipeline(int u, int ue, Load&& load, Compute&& c
 }
 
 // ============================================================== helper wave
+// Argmax of whole tiles: for the first kLaneBest<MM> activation rows each lane
+// keeps the largest value of its own rows (the high half of the argmax key, in
+// a register) and the row that gave it (in LDS, lbi), updated only on a
+// strictly larger value, so among equal values the first row in stream order
+// (the lowest) stays; the pairs are folded into kb once at the end. The other
+// activation rows fold each tile at once (the registers run out: 16 rows fit
+// up to 32 activation rows, none beyond).
+template <int MM>
+constexpr int kLaneBest = MM <= 16 ? MM : MM <= 32 ? 16 : 0;
+template <int MM>
+constexpr int kLaneBestN = kLaneBest<MM> > 0 ? kLaneBest<MM> : 1;  // array extent
+
 // Per-segment state the helper keeps in LDS, in slot (segment index % 3):
 // the segment's plain sums A [m][row], its corrections CN and CP, and its
 // rows' scales; plus the work list of the corrections.
@@ -295,6 +307,7 @@ struct HelperLds {
   // not -1), and the sums of the fin_n split tiles this workgroup is last on.
   uint32_t fin;
   int fin_si, fin_n, fin_t[2], fin_pa[2], fin_pb[2];
+  uint32_t lbi[kLaneBestN<MM>][64];  // argmax: row of each lane's best value per activation row
 };
 
 // Handshakes between the streaming waves and the helper through LDS counters
@@ -566,30 +579,44 @@ __device__ __forceinline__ void argmax_tile64(unsigned long long& kb, float v, b
   }
 }
 
-// Argmax of whole tiles: each lane keeps the best key of its own rows per
-// activation row (lb), folded into kb once at the end (up to 16 activation
-// rows; beyond that the registers run out and each tile is folded at once).
-constexpr int kLaneBestRows = 16;
 
 // Whole-tile segment si (slot si % 3), lane = row: its outputs or argmax keys.
 template <int MM, int ROWS>
 __device__ __forceinline__ void emit_whole(const GemmParams& a, HelperLds<MM, ROWS>& h, const SegList& L, int si,
                                            int lane, unsigned long long& kb,
-                                           unsigned long long (&lb)[MM <= kLaneBestRows ? MM : 1]) {
+                                           uint32_t (&lbv)[kLaneBestN<MM>]) {
   const Seg s = seg_at<ROWS / 16>(a, L, si);
   const int sl = si % kSlots, n0 = s.row0;
   const bool valid = lane < s.rg * 16 && lane < ROWS;
   const int r = lane < ROWS ? lane : ROWS - 1;
   constexpr int C = MM < 16 ? MM : 16;
-  if constexpr (MM <= kLaneBestRows) {
+  constexpr int LB = kLaneBest<MM>;
+  if constexpr (LB > 0) {
     if (a.mode == kModeArgmax) {
 #pragma unroll
-      for (int m0 = 0; m0 < MM; m0 += C) {
+      for (int m0 = 0; m0 < LB; m0 += C) {
         float v[C];
         seg_values<C, 1>(h, sl, r, m0, v);
 #pragma unroll
-        for (int j = 0; j < C; ++j)
-          lb[m0 + j] = max_u64(lb[m0 + j], valid ? argmax_key(v[j], (uint32_t)(n0 + lane)) : 0ull);
+        for (int j = 0; j < C; ++j) {
+          const uint32_t hv = valid ? (uint32_t)(argmax_key(v[j], 0u) >> 32) : 0u;
+          if (hv > lbv[m0 + j]) {
+            lbv[m0 + j] = hv;
+            h.lbi[m0 + j][lane] = (uint32_t)(n0 + lane);
+          }
+        }
+      }
+      if constexpr (LB < MM) {
+#pragma unroll 1
+        for (int m0 = LB; m0 < MM; m0 += C) {
+          if (m0 < a.m) {
+            float v[C];
+            seg_values<C, 1>(h, sl, r, m0, v);
+#pragma unroll
+            for (int j = 0; j < C; ++j)
+              if (m0 + j < a.m) argmax_tile64(kb, v[j], valid, n0, m0 + j, lane);
+          }
+        }
       }
       return;
     }
@@ -920,9 +947,9 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
   __builtin_amdgcn_s_setprio(3);
   constexpr int GB = ROWS / 16;  // 16-row blocks of a whole tile
   unsigned long long kb = 0ull;  // argmax: lane m's best key of activation row m
-  unsigned long long lb[MM <= kLaneBestRows ? MM : 1];  // argmax: this lane's rows' best key per activation row
+  uint32_t lbv[kLaneBestN<MM>];  // argmax: this lane's best value per activation row (0: none)
 #pragma unroll
-  for (int m = 0; m < (MM <= kLaneBestRows ? MM : 1); ++m) lb[m] = 0ull;
+  for (int m = 0; m < kLaneBestN<MM>; ++m) lbv[m] = 0u;
   const int n = L.n;
   const Tgt z{0, 0, 0, 0, 0};
   int corr_end = 0;  // segments [0, corr_end) have their corrections
@@ -976,7 +1003,7 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
     const bool shared = b1 == n && store;
     Xch X{0, 0, 0, 0, 0, 0, 0, 0ull};
     if (split) X = xch_begin<MM, ROWS, TS>(a, h, L, p, b0, b1, lane);
-    else if (!shared) emit_whole<MM, ROWS>(a, h, L, b0, lane, kb, lb);
+    else if (!shared) emit_whole<MM, ROWS>(a, h, L, b0, lane, kb, lbv);
     if ((defer || shared) && split) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -1000,10 +1027,14 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
     b0 = b1;
   }
   if (a.mode == kModeArgmax) {
-    if constexpr (MM <= kLaneBestRows) {
+    if constexpr (kLaneBest<MM> > 0) {
 #pragma unroll
-      for (int m = 0; m < MM; ++m)
-        if (m < a.m) argmax_absorb<64>(kb, lb[m], m, lane);
+      for (int m = 0; m < kLaneBest<MM>; ++m)
+        if (m < a.m) {
+          const unsigned long long key =
+              lbv[m] ? ((unsigned long long)lbv[m] << 32 | (0xFFFFFFFFu - h.lbi[m][lane])) : 0ull;
+          argmax_absorb<64>(kb, key, m, lane);
+        }
     }
     finish_argmax(a, p, lane, kb);
   }

@@ -250,7 +250,7 @@ def test_lmhead_argmax_small(m):
     del rng
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 16, 17, 33, 48, 64])
+@pytest.mark.parametrize("m", [1, 2, 3, 16, 17, 32, 33, 48, 64])
 def test_lmhead_argmax_whole_tiles(m):
     """Enough rows that every workgroup also owns whole tiles (the per-lane and
     per-tile argmax folds), with exact ties planted in different whole tiles:
