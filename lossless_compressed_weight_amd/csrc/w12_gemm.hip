@@ -224,6 +224,15 @@ __device__ __forceinline__ void argmax_absorb(unsigned long long& kb, unsigned l
   }
 }
 
+// Each lane: the largest value of its 16-lane row (DPP row rotations). All lanes active.
+__device__ __forceinline__ uint32_t row_ror_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x121, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x122, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));
+  return v;
+}
+
 // -------------------------------------------------------------- escapes
 // The helper gathers the escape corrections of up to three segments in three
 // memory round trips for up to a few hundred entries: the row pointers of the
@@ -274,17 +283,22 @@ __device__ __forceinline__ void pipeline(int u, int ue, Load&& load, Compute&& c
 }
 
 // ============================================================== helper wave
-// Argmax of whole tiles: for the first kLaneBest<MM> activation rows each lane
+// Argmax of whole tiles: for up to 16 activation rows each lane
 // keeps the largest value of its own rows (the high half of the argmax key, in
 // a register) and the row that gave it (in LDS, lbi), updated only on a
 // strictly larger value, so among equal values the first row in stream order
-// (the lowest) stays; the pairs are folded into kb once at the end. The other
-// activation rows fold each tile at once (the registers run out: 16 rows fit
-// up to 32 activation rows, none beyond).
+// (the lowest) stays; the pairs are folded into kb once at the end. Beyond 16
+// activation rows the registers run out (the kernels for 17..32 rows sit at
+// the 256-register limit) and each tile is folded at once.
 template <int MM>
-constexpr int kLaneBest = MM <= 16 ? MM : MM <= 32 ? 16 : 0;
+constexpr int kLaneBest = MM <= 16 ? MM : 0;
 template <int MM>
 constexpr int kLaneBestN = kLaneBest<MM> > 0 ? kLaneBest<MM> : 1;  // array extent
+// Row length (elements) of the escape activation staging area: rows of a
+// multiple of 8 activations get 16 bytes of padding, so that 16-byte accesses
+// of eight consecutive lanes (one row each) fall in different LDS banks.
+template <int MM>
+constexpr int kStageRow = MM % 8 == 0 ? MM + 8 : MM;
 
 // Per-segment state the helper keeps in LDS, in slot (segment index % 3):
 // the segment's plain sums A [m][row], its corrections CN and CP, and its
@@ -308,6 +322,10 @@ struct HelperLds {
   uint32_t fin;
   int fin_si, fin_n, fin_t[2], fin_pa[2], fin_pb[2];
   uint32_t lbi[kLaneBestN<MM>][64];  // argmax: row of each lane's best value per activation row
+  // escapes, up to 32 activation rows: a pass's activations [entry][activation row],
+  // its run starts and then its entry count
+  alignas(16) uint16_t xs[MM <= 32 ? 64 : 1][kStageRow<MM>];
+  int rs[MM <= 32 ? 65 : 1];
 };
 
 // Handshakes between the streaming waves and the helper through LDS counters
@@ -336,15 +354,24 @@ __device__ __forceinline__ int rp_row(const uint32_t* rp, int rows, uint32_t j) 
   return lo;
 }
 
-// Add the listed entries [0, n) to the corrections, 64 at a time with
-// lane = entry. Entries come sorted by (target, row, column), so each row's
-// entries of a pass are a run of lanes; in round k the k-th entry of every run
-// adds its products to its row's sums, so no two lanes of a round touch the
-// same sums and every row's sums grow in column order (a run split across
-// passes continues in the next pass). The activations of PB passes' entries
-// are gathered in one round trip and stay in registers: from the transposed
-// copy when there is one (XT, one line per entry), else from x (one load per
-// activation row).
+// Add the listed entries [0, n) to the corrections, 64 at a time. Entries
+// come sorted by (target, row, column), so each row's entries of a pass are a
+// run of lanes, and every row's sums must grow in column order, one fused
+// multiply-add per entry (a run split across passes continues in the next
+// pass). Two ways give the same sums bit for bit; each pass takes the cheaper:
+// - rounds: lane = entry; in round k the k-th entry of every run adds its
+//   products to its row's sums in LDS. L rounds (L: the longest run), each a
+//   dependent LDS read-modify-write of 2 MM sums: good for many short runs;
+// - runs: the pass's activations are staged in LDS; each run gets G lanes, one
+//   per activation row, that walk its entries in order with the sums in
+//   registers. ceil(R / (64 / G)) groups of runs (R: the runs), each about
+//   L / 8 LDS round trips: good for few long runs (dense escape rows).
+// The activations of PB passes' entries are gathered in one round trip and
+// stay in registers: from the transposed copy when there is one (XT, one line
+// per entry), else from x (one load per activation row).
+template <int MM>
+constexpr int kRunLanes = MM <= 1 ? 1 : MM <= 2 ? 2 : MM <= 4 ? 4 : MM <= 8 ? 8 : MM <= 16 ? 16 : MM <= 32 ? 32 : 64;
+
 template <int MM, int ROWS, bool XT>
 __device__ __forceinline__ void esc_passes(const GemmParams& a, HelperLds<MM, ROWS>& h, int n, int slot0,
                                            int slot1, int slot2, int lane) {
@@ -357,6 +384,7 @@ __device__ __forceinline__ void esc_passes(const GemmParams& a, HelperLds<MM, RO
   constexpr int LB = XT ? (MM > 32 ? 8 : 16) : (MM > 32 ? 64 : 2 * MM > 16 ? 2 * MM : 16);
   constexpr int PB = LP >= LB ? 1 : (LB / LP > kEscLoad<MM> ? kEscLoad<MM> : LB / LP);
   constexpr int C = MM < 16 ? MM : 16;  // activation rows per batch of LDS reads
+  constexpr int G = kRunLanes<MM>, RPG = 64 / G;
   for (int e00 = 0; e00 < n; e00 += 64 * PB) {
     // XT: the entry's activations for all rows, one line of the transposed
     // copy (rows past M are zero there); otherwise one load per row (rows
@@ -383,13 +411,75 @@ __device__ __forceinline__ void esc_passes(const GemmParams& a, HelperLds<MM, RO
         const int ne = min(64, n - e0);
         const bool live = lane < ne;
         const int e = e0 + (live ? lane : 0);
-        const uint32_t bits = h.ebits[e];
         const uint32_t tr = live ? h.erow[e] : 0xFFFFFFFFu;
         const uint32_t tp = lane > 0 ? h.erow[max(e - 1, 0)] : 0xFFFFFFFEu;
         const bool head = live && (lane == 0 || tp != tr);
+        const uint64_t H = __ballot(head);
         // position in the run: lanes since the closest head at or below this lane
-        const uint64_t below = __ballot(head) & (lane == 63 ? ~0ull : (2ull << lane) - 1ull);
+        const uint64_t below = H & (lane == 63 ? ~0ull : (2ull << lane) - 1ull);
         const int pos = below ? lane - (63 - __clzll(below)) : 0;
+        // the runs and the longest one (uniform)
+        const int R = __popcll(H);
+        const uint32_t lmax = row_ror_max_u32(live ? (uint32_t)pos + 1u : 0u);
+        const int L = (int)max(max((uint32_t)__builtin_amdgcn_readlane((int)lmax, 0),
+                                   (uint32_t)__builtin_amdgcn_readlane((int)lmax, 16)),
+                               max((uint32_t)__builtin_amdgcn_readlane((int)lmax, 32),
+                                   (uint32_t)__builtin_amdgcn_readlane((int)lmax, 48)));
+        // estimated cycles of each way (an LDS round trip ~150 cycles)
+        const int cost_rounds = L * (150 + 6 * MM);
+        const int cost_runs = ((R + RPG - 1) / RPG) * (((L + 7) >> 3) * 150 + 8 * L) + 4 * MM;
+        // (beyond 32 activation rows only the rounds: the kernels have no registers to spare)
+        if constexpr (MM <= 32) {
+          if (cost_runs < cost_rounds) {
+            // runs: stage the activations [entry][activation row] and the run
+            // starts, then each run's lanes walk its entries
+#pragma unroll
+            for (int m0 = 0; m0 < MM; m0 += 8) {
+              if constexpr (XT) {
+                *reinterpret_cast<uint4*>(&h.xs[lane][m0]) = xq[pp][m0 / 8];
+              } else {
+#pragma unroll
+                for (int m = m0; m < m0 + 8 && m < MM; ++m) h.xs[lane][m] = xg[pp][m];
+              }
+            }
+            if (head) h.rs[__builtin_amdgcn_mbcnt_hi((uint32_t)(H >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)H, 0u))] = lane;
+            if (lane == 0) h.rs[R] = ne;
+            __builtin_amdgcn_wave_barrier();
+            for (int g0 = 0; g0 < R; g0 += RPG) {
+              const int j = g0 + lane / G, m = lane % G;
+              if (j < R && m < MM) {
+                const int q0 = h.rs[j], q1 = h.rs[j + 1];
+                const uint32_t row = h.erow[e0 + q0];
+                const uint32_t sl = (slots >> (4 * ((row >> 8) & 3u))) & 15u, r = row & 255u;
+                float cn = h.cn[sl][m][r], cp = h.cp[sl][m][r];
+                for (int q = q0; q < q1; q += 8) {
+                  // eight entries' loads first, then their products in order
+                  uint32_t bb[8];
+                  uint16_t xx[8];
+#pragma unroll
+                  for (int i = 0; i < 8; ++i) {
+                    const int qi = min(q + i, q1 - 1);
+                    bb[i] = h.ebits[e0 + qi];
+                    xx[i] = h.xs[qi][m];
+                  }
+#pragma unroll
+                  for (int i = 0; i < 8; ++i) {
+                    if (q + i < q1) {
+                      const float x = bf16_to_f32(xx[i]);
+                      cn = fmaf(x, esc_placeholder(a, bb[i]), cn);
+                      cp = fmaf(x, bf16_to_f32(bb[i] & 0xFFFFu), cp);
+                    }
+                  }
+                }
+                h.cn[sl][m][r] = cn;
+                h.cp[sl][m][r] = cp;
+              }
+            }
+            __builtin_amdgcn_wave_barrier();
+            continue;
+          }
+        }
+        const uint32_t bits = h.ebits[e];
         const float ph = esc_placeholder(a, bits), ex = bf16_to_f32(bits & 0xFFFFu);
         const uint32_t sl = (slots >> (4 * ((tr >> 8) & 3u))) & 15u, r = live ? tr & 255u : 0u;
         float xv[MM];
@@ -406,7 +496,7 @@ __device__ __forceinline__ void esc_passes(const GemmParams& a, HelperLds<MM, RO
             if (m + 1 < MM) xv[m + 1] = bf16_to_f32(xg[pp][m + 1 < MM ? m + 1 : m]);
           }
         }
-        for (int k = 0; __ballot(live && pos >= k) != 0; ++k) {
+        for (int k = 0; k < L; ++k) {
           if (live && pos == k) {
 #pragma unroll
             for (int m0 = 0; m0 < MM; m0 += C) {
@@ -559,14 +649,6 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long ke
 // tile's best key into lane m's kb. The value half of the keys is reduced
 // first (DPP row maxima, then the four rows); the lowest valid lane holding
 // it gives the index half, so ties go to the lowest row. All lanes active.
-__device__ __forceinline__ uint32_t row_ror_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x121, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x122, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));
-  return v;
-}
-
 __device__ __forceinline__ void argmax_tile64(unsigned long long& kb, float v, bool valid, int n0, int m, int lane) {
   const uint32_t hi = valid ? (uint32_t)(argmax_key(v, 0u) >> 32) : 0u;
   const uint32_t rm = row_ror_max_u32(hi);
@@ -593,12 +675,13 @@ __device__ __forceinline__ void emit_whole(const GemmParams& a, HelperLds<MM, RO
   constexpr int LB = kLaneBest<MM>;
   if constexpr (LB > 0) {
     if (a.mode == kModeArgmax) {
+      constexpr int CL = LB < C ? LB : C;
 #pragma unroll
-      for (int m0 = 0; m0 < LB; m0 += C) {
-        float v[C];
-        seg_values<C, 1>(h, sl, r, m0, v);
+      for (int m0 = 0; m0 < LB; m0 += CL) {
+        float v[CL];
+        seg_values<CL, 1>(h, sl, r, m0, v);
 #pragma unroll
-        for (int j = 0; j < C; ++j) {
+        for (int j = 0; j < CL; ++j) {
           const uint32_t hv = valid ? (uint32_t)(argmax_key(v[j], 0u) >> 32) : 0u;
           if (hv > lbv[m0 + j]) {
             lbv[m0 + j] = hv;
