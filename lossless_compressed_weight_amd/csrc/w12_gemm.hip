@@ -425,12 +425,14 @@ __device__ __forceinline__ void esc_passes(const GemmParams& a, HelperLds<MM, RO
                                    (uint32_t)__builtin_amdgcn_readlane((int)lmax, 16)),
                                max((uint32_t)__builtin_amdgcn_readlane((int)lmax, 32),
                                    (uint32_t)__builtin_amdgcn_readlane((int)lmax, 48)));
-        // estimated cycles of each way (an LDS round trip ~150 cycles)
+        // estimated cycles of each way (an LDS round trip ~150 cycles); the
+        // runs must win by 4x, as the estimate flatters them on short runs
+        // (measured: 1 us per call on a normal matrix at M = 32 with 1x)
         const int cost_rounds = L * (150 + 6 * MM);
         const int cost_runs = ((R + RPG - 1) / RPG) * (((L + 7) >> 3) * 150 + 8 * L) + 4 * MM;
         // (beyond 32 activation rows only the rounds: the kernels have no registers to spare)
         if constexpr (MM <= 32) {
-          if (cost_runs < cost_rounds) {
+          if (4 * cost_runs < cost_rounds) {
             // runs: stage the activations [entry][activation row] and the run
             // starts, then each run's lanes walk its entries
 #pragma unroll
