@@ -46,11 +46,94 @@ def parse():
     ap.add_argument("--cpu-passes", type=int, default=2, help="passes of the oracle over its sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--ms", type=str, default=None, help="comma-separated M values (default 1,32)")
+    ap.add_argument("--probe-sweep", type=str, default=None,
+                    help="run only the read-bandwidth probe over its parameter grid; JSON lines to this file")
     return ap.parse_args()
+
+
+PROBE_REGION = 17408 * 5120 * 3 // 2   # bytes of one packed 17408 x 5120 W12 matrix
+PROBE_REGIONS = 16                     # 2.1 GB rotated, far above the 256 MB last-level cache
+
+
+def probe_time(w12, buf, nbytes, grid, block, loads, mode, ws, stream, reps=12, warm=2, stamps=None):
+    """Per-launch times (us) of the probe reading `nbytes`, each launch on the
+    next of the buffer's regions (so no launch finds its bytes in a cache)."""
+    import torch
+    nreg = buf.numel() // nbytes
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(warm + reps):
+        view = buf[(i % nreg) * nbytes:]
+        if i >= warm:
+            ev[i - warm][0].record(stream)
+        w12.w12_probe_read(view, nbytes, grid, block, loads, mode, stamps if i == warm + reps - 1 else None, ws,
+                           stream)
+        if i >= warm:
+            ev[i - warm][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def probe_sweep(path):
+    """Read-bandwidth probe over workgroups per CU, waves per workgroup, loads
+    in flight per lane and the work distribution, on 134 MB reads (one packed
+    17408 x 5120 matrix) rotated over 2.1 GB; then the best setting on one
+    1.17 GB read (the packed LM head) and with per-workgroup time stamps."""
+    import torch
+    from lossless_compressed_weight_amd import w12
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    buf = torch.zeros(PROBE_REGION * PROBE_REGIONS, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(w12.PROBE_WS_BYTES, dtype=torch.uint8, device=dev)
+    out = open(path, "w")
+    best = None
+    for mode in (w12.PROBE_STATIC, w12.PROBE_DYNAMIC, w12.PROBE_STRIDE):
+        for block in (256, 512, 1024):
+            for wgpc in (1, 2, 4):
+                for loads in (1, 2, 4, 8):
+                    t = probe_time(w12, buf, PROBE_REGION, 256 * wgpc, block, loads, mode, ws, stream)
+                    med = float(np.median(t))
+                    rec = {"mode": mode, "block": block, "wg_per_cu": wgpc, "loads": loads,
+                           "us_median": round(med, 3), "us_min": round(min(t), 3),
+                           "gbs": round(PROBE_REGION / med / 1e3, 1)}
+                    out.write(json.dumps(rec) + "\n")
+                    out.flush()
+                    if best is None or med < best[0]:
+                        best = (med, rec)
+    print(f"# probe best on 134 MB: {best[1]}", file=sys.stderr, flush=True)
+    # time stamps: spread of workgroup start and end times for each mode at the best occupancy
+    b = best[1]
+    for mode in (w12.PROBE_STATIC, w12.PROBE_DYNAMIC, w12.PROBE_STRIDE):
+        grid = 256 * b["wg_per_cu"]
+        st = torch.zeros(3 * grid, dtype=torch.int64, device=dev)
+        t = probe_time(w12, buf, PROBE_REGION, grid, b["block"], b["loads"], mode, ws, stream, stamps=st)
+        a = st.cpu().numpy().reshape(grid, 3).astype(np.int64)
+        t0 = a[:, 0].min()
+        start, end = (a[:, 0] - t0) * 0.01, (a[:, 1] - t0) * 0.01   # 100 MHz counter -> us
+        per_xcd = {int(x): round(float(end[a[:, 2] == x].max()), 3) for x in np.unique(a[:, 2])}
+        rec = {"stamps_mode": mode, "grid": grid, "block": b["block"], "loads": b["loads"],
+               "us_median": round(float(np.median(t)), 3),
+               "start_us": [round(float(np.percentile(start, q)), 3) for q in (0, 50, 100)],
+               "end_us": [round(float(np.percentile(end, q)), 3) for q in (0, 10, 50, 90, 100)],
+               "last_end_per_xcd_us": per_xcd}
+        out.write(json.dumps(rec) + "\n")
+        out.flush()
+    # one LM-head-sized read
+    big = 151936 * 5120 * 3 // 2
+    big -= big % 16
+    for mode in (w12.PROBE_STATIC, w12.PROBE_DYNAMIC):
+        t = probe_time(w12, buf, big, 256 * b["wg_per_cu"], b["block"], b["loads"], mode, ws, stream, reps=4)
+        rec = {"lm_head_bytes": big, "mode": mode, "us_median": round(float(np.median(t)), 3),
+               "gbs": round(big / float(np.median(t)) / 1e3, 1)}
+        out.write(json.dumps(rec) + "\n")
+    out.close()
 
 
 def main():
     args = parse()
+    if args.probe_sweep:
+        probe_sweep(args.probe_sweep)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the W12 GEMM shards along output channels with no exchange; see the design notes)",

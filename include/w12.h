@@ -158,8 +158,8 @@ int w12_decode(const w12_matrix* m, uint16_t* w_out, void* stream);
  * x: BF16, row stride ldx >= K elements (a multiple of 8, at most 2^25),
  *    16-byte aligned rows.
  * y: BF16 or fp32 (y_dtype), row stride ldy >= N elements (below 2^31).
- * 1 <= M <= 64: M <= 2 runs the wavefront GEMV kernel, M >= 3 the MFMA kernel
- * (M padded to a multiple of 16).
+ * 1 <= M <= 64: M <= 2 runs the lane-per-row GEMV kernel, M >= 3 an MFMA
+ * kernel (M padded to a multiple of 16); w12_plan_info names the kernel.
  * ws: w12_workspace_bytes(W12_OP_GEMM, n, k, M) bytes (device). */
 int w12_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,
              int y_dtype, void* ws, size_t ws_bytes, void* stream);
@@ -186,14 +186,54 @@ int w12_lmhead_argmax(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t
  * ws: 4 bytes of device memory. Returns W12_OK or W12_E_CORRUPT. */
 int w12_validate(const w12_matrix* m, void* ws, size_t ws_bytes, void* stream);
 
-/* Test and tuning hooks (process-wide, not thread-safe; call before launching).
- * W12_TUNE_PATH: 0 = choose by M, 1 = force the GEMV kernel (M <= 16),
- *   2 = force the MFMA kernel.
+/* The GEMM kernels (w12_plan.kernel and W12_TUNE_PATH values).
+ * GEMV: one lane per matrix row, activations as scalar operands (M <= 2 by
+ *   default; any M <= 16 when forced).
+ * MFMA_HELPER: v_mfma_f32_16x16x32_bf16 with four streaming waves and a
+ *   helper wave that applies the escape corrections; an activation transpose
+ *   kernel runs first. Used for the fused LM-head argmax, for matrices with
+ *   more than 8 escapes per row on average, and for K > 2^20.
+ * MFMA_STREAM: v_mfma_f32_16x16x32_bf16 with eight streaming waves, escapes
+ *   substituted into the decoded weights in registers, activations read
+ *   straight from x; no pre-pass. The default for 3 <= M <= 64 otherwise. */
+#define W12_KERNEL_GEMV 1
+#define W12_KERNEL_MFMA_HELPER 2
+#define W12_KERNEL_MFMA_STREAM 3
+
+/* The plan of one GEMM call (host-side description; nothing is launched). */
+typedef struct {
+  int32_t kernel;          /* W12_KERNEL_*                                             */
+  int32_t grid;            /* workgroups of the GEMM kernel                            */
+  int32_t threads;         /* threads per workgroup                                    */
+  int32_t tile_rows;       /* rows of a whole tile                                     */
+  int32_t whole_tiles;     /* whole tiles per workgroup                                */
+  int32_t split_tiles;     /* tiles whose columns several workgroups share (stream-K)  */
+  int32_t split_tile_rows; /* rows of a split tile                                     */
+  int32_t unit_cols;       /* columns of a stream-K unit                               */
+  int64_t split_units;     /* units of the split tiles                                 */
+  int32_t prepass;         /* 1: an activation transpose kernel runs before the GEMM   */
+  int32_t reserved;
+  size_t workspace_bytes;  /* what this plan uses (w12_workspace_bytes covers them all) */
+} w12_plan;
+
+/* The plan w12_gemm (op W12_OP_GEMM), w12_gemm_q8 (W12_OP_GEMM_Q8, with its
+ * flags) or w12_lmhead_argmax (W12_OP_LMHEAD_ARGMAX) would run for matrix m
+ * and M activation rows. Host-only: reads m->n, m->k and m->n_esc, touches no
+ * device memory. Returns W12_OK or the status the call would return for
+ * these arguments. */
+int w12_plan_info(const w12_matrix* m, int op, int64_t M, uint32_t flags, w12_plan* out);
+
+/* Test hooks, per calling thread (other threads' calls are unaffected).
+ * W12_TUNE_PATH: 0 = the library's choice, 1 = the GEMV kernel (M <= 16),
+ *   2 = the MFMA helper-wave kernel, 3 = the MFMA stream kernel (where it
+ *   applies; the fused argmax always runs the helper-wave kernel).
  * W12_TUNE_GRID: workgroup count for the GEMM kernels (0 = the library's
  *   choice: 256, or c * T for a matrix of T < 256 tiles; at most 4096 and at
  *   most the number of work units are used).
- * Changing W12_TUNE_GRID changes the fp32 summation order and the workspace
- * size; query w12_workspace_bytes after setting it. Returns the old value. */
+ * A hook changes which kernel runs or how K is split, so the fp32 summation
+ * order and the workspace size; query w12_workspace_bytes after setting it.
+ * With the hooks at 0, results depend only on the matrix, x, N, K and M.
+ * Returns the old value. */
 #define W12_TUNE_PATH 1
 #define W12_TUNE_GRID 2
 int64_t w12_set_tuning(int key, int64_t value);

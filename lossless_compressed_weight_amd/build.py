@@ -9,13 +9,14 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libw12.so")
-SOURCES = ["w12_api.hip", "w12_encode.hip", "w12_gemm.hip"]
+SOURCES = ["w12_gemm.hip", "w12_gemm_mx.hip", "w12_api.hip", "w12_encode.hip", "w12_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -36,12 +37,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the W12 library needs ROCm's hipcc to build")
 
 
+def _jobs() -> int:
+    try:
+        return max(1, min(16, int(os.environ.get("MAX_JOBS", "0")) or (os.cpu_count() or 1)))
+    except ValueError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libw12.so next to this file."""
+    """Compile every source for gfx950 (in parallel) and link libw12.so next to this file."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="w12build") as tmp:
-        objs = []
-        for src in SOURCES:
+        def compile_one(src):
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             cmd = [cc, *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
@@ -49,7 +56,10 @@ def build(verbose: bool = False) -> str:
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-            objs.append(obj)
+            return obj
+
+        with ThreadPoolExecutor(_jobs()) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
         tmp_lib = LIB + ".tmp"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -12,8 +12,15 @@ using namespace w12;
 namespace {
 
 thread_local std::string g_last_error;
-int g_tune_path = 0;
-int64_t g_tune_grid = 0;
+// Test hooks (w12_set_tuning): per thread, so that a test forcing a kernel
+// or a grid never changes what another thread's calls compute.
+thread_local int g_tune_path = 0;
+thread_local int64_t g_tune_grid = 0;
+
+// The stream kernel takes matrices whose escapes are sparse enough for its
+// per-wave substitution lists: at most this many escapes per row on average
+// (the synthetic workloads have about 1.4; the escape-stress workload 56).
+constexpr int64_t kMxMaxEscPerRow = 8;
 
 int hip_fail(hipError_t e, const char* where) {
   g_last_error = std::string(where) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
@@ -55,20 +62,78 @@ int check_gemm_args(const w12_matrix* m, const void* x, int64_t M, int64_t ldx, 
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// workspace: [counters | partial slots | argmax keys | transposed x | x in
-// MFMA operand order], each 256-byte aligned
+// workspace of the helper-wave kernels: [counters | partial slots | argmax
+// keys | transposed x | x in MFMA operand order], each 256-byte aligned
 size_t gemm_ws_bytes(const GemmPlan& pl) {
   return round256(pl.ctr_bytes) + round256(pl.part_bytes) + round256(pl.key_bytes) + round256(pl.xt_bytes) +
          round256(pl.xk_bytes);
 }
 
+// workspace of the stream kernel: [counters | partial slots]
+size_t mx_ws_bytes(const MxPlan& pl) { return round256(kCounterBytes) + round256(pl.part_bytes); }
+
 GemmPlan make_plan(int64_t n, int64_t k, int64_t M, int op) {
-  return plan_gemm(n, k, M, op, g_tune_path, g_tune_grid);
+  return plan_gemm(n, k, M, op, g_tune_path == 3 ? 2 : g_tune_path, g_tune_grid);
+}
+
+// The kernel a call runs: the lane-per-row GEMV for M <= 2, otherwise the
+// stream MFMA kernel, except for the fused argmax, matrices with dense
+// escapes and very long rows, which run the helper-wave MFMA kernel.
+int choose_kernel(int64_t n, int64_t k, int64_t n_esc, int64_t M, int op, bool fix, const GemmPlan& old) {
+  const bool mx_ok = op != W12_OP_LMHEAD_ARGMAX && k <= kMxMaxK;
+  if (g_tune_path == 1) return W12_KERNEL_GEMV;
+  if (g_tune_path == 2) return W12_KERNEL_MFMA_HELPER;
+  if (g_tune_path == 3) return mx_ok ? W12_KERNEL_MFMA_STREAM : W12_KERNEL_MFMA_HELPER;
+  if (!old.mfma) return W12_KERNEL_GEMV;
+  if (mx_ok && (!fix || n_esc <= kMxMaxEscPerRow * n)) return W12_KERNEL_MFMA_STREAM;
+  (void)M;
+  return W12_KERNEL_MFMA_HELPER;
+}
+
+// Every plan a GEMM op may run for this shape fits in this much workspace.
+size_t ws_bytes_any(int64_t n, int64_t k, int64_t M, int op) {
+  size_t b = gemm_ws_bytes(make_plan(n, k, M, op));
+  if (op != W12_OP_LMHEAD_ARGMAX && k <= kMxMaxK) {
+    const size_t bx = mx_ws_bytes(plan_mx(n, k, M, g_tune_grid));
+    if (bx > b) b = bx;
+  }
+  return b;
+}
+
+int run_mx(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
+           int op, bool fix, void* ws, size_t ws_bytes, void* stream) {
+  const MxPlan pl = plan_mx(m->n, m->k, M, g_tune_grid);
+  const size_t need = mx_ws_bytes(pl);
+  if (!ws || ws_bytes < need) return W12_E_WORKSPACE;
+  MxParams p{};
+  p.rec = m->records;
+  p.e_top = m->e_top;
+  p.row_ptr = m->esc_row_ptr;
+  p.esc = reinterpret_cast<const uint2*>(m->esc);
+  p.x = x;
+  p.ldx = ldx;
+  p.y = y;
+  p.ldy = ldy;
+  char* wsb = reinterpret_cast<char*>(ws);
+  p.ctr = reinterpret_cast<uint32_t*>(wsb);
+  p.part = reinterpret_cast<float*>(wsb + round256(kCounterBytes));
+  p.n = (int)m->n;
+  p.k = (int)m->k;
+  p.kb = (int)(m->k / W12_REC_COLS);
+  p.m = (int)M;
+  p.y_f32 = y_dtype == W12_F32;
+  p.fix = fix && m->n_esc > 0;
+  p.q = op == W12_OP_GEMM_Q8;
+  const hipError_t e = launch_mx(pl, p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return W12_OK;
 }
 
 int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
              int op, bool fix, void* ws, size_t ws_bytes, int32_t* idx, float* maxv, void* stream) {
   const GemmPlan pl = make_plan(m->n, m->k, M, op);
+  const int kernel = choose_kernel(m->n, m->k, m->n_esc, M, op, fix, pl);
+  if (kernel == W12_KERNEL_MFMA_STREAM) return run_mx(m, x, M, ldx, y, ldy, y_dtype, op, fix, ws, ws_bytes, stream);
   if (!pl.mfma && M > 16) return W12_E_M_RANGE;
   const size_t need = gemm_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return W12_E_WORKSPACE;
@@ -97,13 +162,12 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   p.fix = fix && m->n_esc > 0;
   p.q = op == W12_OP_GEMM_Q8;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // The MFMA kernel's escape fix-up needs the activations of each escape
-  // column for all rows. With many escapes per row it reads them from a
-  // transposed copy of x (one cache line per escape instead of one per
-  // activation row), at the price of one more kernel; with few it gathers
-  // them from x directly.
-  // The MFMA kernel also reads its B operands from a copy of x in operand
-  // order (fully coalesced loads); one kernel writes both copies.
+  // The helper-wave MFMA kernel's escape fix-up needs the activations of each
+  // escape column for all rows. With many escapes per row it reads them from
+  // a transposed copy of x (one cache line per escape instead of one per
+  // activation row), with few it gathers them from x directly. It also reads
+  // its B operands from a copy of x in operand order (fully coalesced loads);
+  // one kernel writes both copies before it.
   p.xt = nullptr;
   p.xk = nullptr;
   if (pl.mfma) {
@@ -163,7 +227,48 @@ size_t w12_workspace_bytes(int op, int64_t n, int64_t k, int64_t m) {
   if (op == W12_OP_ENCODE_PLAN) return round256((size_t)n * sizeof(uint32_t));
   if (op != W12_OP_GEMM && op != W12_OP_GEMM_Q8 && op != W12_OP_LMHEAD_ARGMAX) return 0;
   if (m < 1 || m > W12_MAX_M) return 0;
-  return gemm_ws_bytes(make_plan(n, k, m, op));
+  return ws_bytes_any(n, k, m, op);
+}
+
+int w12_plan_info(const w12_matrix* m, int op, int64_t M, uint32_t flags, w12_plan* out) {
+  if (!m || !out) return W12_E_INVALID_ARG;
+  const int s = check_shape(m->n, m->k);
+  if (s != W12_OK) return s;
+  if (m->n_esc < 0 || m->n_esc > m->n * m->k) return W12_E_INVALID_ARG;
+  if (op != W12_OP_GEMM && op != W12_OP_GEMM_Q8 && op != W12_OP_LMHEAD_ARGMAX) return W12_E_INVALID_ARG;
+  if (M < 1 || M > W12_MAX_M) return W12_E_M_RANGE;
+  if (flags & ~W12_Q8_APPLY_ESCAPES) return W12_E_INVALID_ARG;
+  const bool fix = op != W12_OP_GEMM_Q8 || (flags & W12_Q8_APPLY_ESCAPES);
+  const GemmPlan pl = make_plan(m->n, m->k, M, op);
+  w12_plan o{};
+  o.kernel = choose_kernel(m->n, m->k, m->n_esc, M, op, fix, pl);
+  if (o.kernel == W12_KERNEL_MFMA_STREAM) {
+    const MxPlan px = plan_mx(m->n, m->k, M, g_tune_grid);
+    o.grid = px.P;
+    o.threads = 512;
+    o.tile_rows = px.gb * 16;
+    o.whole_tiles = px.dp;
+    o.split_tiles = px.sk_tiles;
+    o.split_tile_rows = px.tb * 16;
+    o.unit_cols = W12_REC_COLS;
+    o.split_units = px.sk_units;
+    o.prepass = 0;
+    o.workspace_bytes = mx_ws_bytes(px);
+  } else {
+    if (!pl.mfma && M > 16) return W12_E_M_RANGE;
+    o.grid = pl.P;
+    o.threads = 320;
+    o.tile_rows = pl.gb * 16;
+    o.whole_tiles = pl.dp;
+    o.split_tiles = pl.sk_tiles;
+    o.split_tile_rows = pl.tile_rows;
+    o.unit_cols = 256;
+    o.split_units = pl.sk_units;
+    o.prepass = pl.mfma ? 1 : 0;
+    o.workspace_bytes = gemm_ws_bytes(pl);
+  }
+  *out = o;
+  return W12_OK;
 }
 
 int w12_encode_plan(const uint16_t* w, int64_t n, int64_t k, uint8_t* e_top, uint32_t* esc_row_ptr,

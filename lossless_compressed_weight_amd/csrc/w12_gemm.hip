@@ -1459,7 +1459,10 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t gr
   if (P < 1) P = 1;
   pl.P = (int)P;
   pl.dp = (int)(tiles / P);
-  const int64_t rem = nb - P * pl.dp * pl.gb;  // blocks left for the split tiles
+  // Blocks left for the split tiles. When P * dp covers every tile and the
+  // last tile is partial (N not a multiple of the tile height), the whole
+  // tiles already reach past N: nothing is left (seg_at clips the last tile).
+  const int64_t rem = nb - P * pl.dp * pl.gb > 0 ? nb - P * pl.dp * pl.gb : 0;
   // Split tiles are whole-tile sized when many rows are left (a few sharers
   // each) and single blocks when few are: a tile shared by many workgroups
   // would leave its last workgroup many partial sums to read. (The GEMV

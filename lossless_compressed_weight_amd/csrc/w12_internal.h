@@ -206,6 +206,50 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t grid_override);
 hipError_t launch_gemm(const GemmPlan& plan, GemmParams p, hipStream_t s, int* unsupported);
+
+// ------------------------------------------------------------------ stream kernel
+// The MFMA stream kernel (w12_gemm_mx.hip): eight streaming waves per
+// workgroup, activations read straight from x, escapes substituted into the
+// decoded weights in registers (exact decode), no helper wave and no
+// activation pre-pass.
+struct MxParams {
+  const uint8_t* rec;
+  const uint8_t* e_top;
+  const uint32_t* row_ptr;
+  const uint2* esc;          // w12_escape as {col, bits | ph << 16}
+  const uint16_t* x;
+  int64_t ldx;
+  void* y;
+  int64_t ldy;
+  uint32_t* ctr;             // split-tile counters [sk_tiles]; zero between calls
+  float* part;               // split slots [2P][MM][tile_rows]
+  int64_t sk_units;          // 512-column units of the split tiles
+  int sk_row0;               // first row of the split tiles
+  int n, k;
+  int kb;                    // records (and units) per 16-row block: K / 512
+  int P;                     // workgroups
+  int dp;                    // whole tiles per workgroup
+  int m;                     // activation rows
+  int y_f32;
+  int fix;                   // substitute the exact escape values
+  int q;                     // Q pass: dropped mantissa bits at their midpoint
+};
+
+struct MxPlan {
+  int P;
+  int gb;         // 16-row blocks of a whole tile
+  int tb;         // 16-row blocks of a split tile
+  int dp;
+  int sk_row0;
+  int sk_tiles;
+  int64_t sk_units;
+  size_t part_bytes;
+};
+// Largest K the stream kernel takes (its per-segment unit count fits the
+// escape bucket arithmetic); larger K runs the helper-wave kernel.
+constexpr int64_t kMxMaxK = (int64_t)1 << 20;
+MxPlan plan_mx(int64_t n, int64_t k, int64_t m, int64_t grid_override);
+hipError_t launch_mx(const MxPlan& plan, MxParams p, hipStream_t s);
 // x [M, K] (row stride ldx) -> xt [K, mm] (mm = 16 * ceil(M / 16)) and xk (MFMA operand order), rows
 // past M zero; either output may be null.
 hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, uint16_t* xt, uint16_t* xk,

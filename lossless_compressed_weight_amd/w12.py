@@ -32,6 +32,8 @@ BF16, F32 = 0, 1
 OP_ENCODE_PLAN, OP_GEMM, OP_GEMM_Q8, OP_LMHEAD_ARGMAX = 1, 2, 3, 4
 Q8_APPLY_ESCAPES = 1
 TUNE_PATH, TUNE_GRID = 1, 2
+KERNEL_GEMV, KERNEL_MFMA_HELPER, KERNEL_MFMA_STREAM = 1, 2, 3
+KERNEL_NAMES = {KERNEL_GEMV: "gemv", KERNEL_MFMA_HELPER: "mfma_helper", KERNEL_MFMA_STREAM: "mfma_stream"}
 
 
 class W12Error(RuntimeError):
@@ -53,6 +55,13 @@ class MatrixC(ctypes.Structure):
                 ("n_esc", ctypes.c_int64), ("format_version", ctypes.c_uint32)]
 
 
+class PlanC(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("grid", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("tile_rows", ctypes.c_int32), ("whole_tiles", ctypes.c_int32), ("split_tiles", ctypes.c_int32),
+                ("split_tile_rows", ctypes.c_int32), ("unit_cols", ctypes.c_int32), ("split_units", ctypes.c_int64),
+                ("prepass", ctypes.c_int32), ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
@@ -70,6 +79,11 @@ _SIGNATURES = {
     "w12_lmhead_argmax": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "w12_validate": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _SZ, _P]),
     "w12_set_tuning": (_I64, [ctypes.c_int, _I64]),
+    "w12_plan_info": (ctypes.c_int, [ctypes.POINTER(MatrixC), ctypes.c_int, _I64, ctypes.c_uint32,
+                                     ctypes.POINTER(PlanC)]),
+    # include/w12_probe.h
+    "w12_probe_read": (ctypes.c_int, [_P, _SZ, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _SZ,
+                                      ctypes.c_int, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -118,6 +132,18 @@ def _ptr(t) -> ctypes.c_void_p:
 
 def set_tuning(key: int, value: int) -> int:
     return int(lib().w12_set_tuning(key, value))
+
+
+def plan_info(mat_or_desc, op: int, m: int, flags: int = 0) -> dict:
+    """The plan the library would run (w12_plan_info): a dict of the w12_plan
+    fields plus the kernel's name. Host-only; accepts a W12Matrix or a
+    MatrixC descriptor (only n, k and n_esc are read)."""
+    d = mat_or_desc.desc() if hasattr(mat_or_desc, "desc") else mat_or_desc
+    out = PlanC()
+    _check(lib().w12_plan_info(ctypes.byref(d), op, m, flags, ctypes.byref(out)), "w12_plan_info")
+    rec = {f: getattr(out, f) for f, _ in PlanC._fields_ if f != "reserved"}
+    rec["kernel_name"] = KERNEL_NAMES.get(out.kernel, "?")
+    return rec
 
 
 def workspace_bytes(op: int, n: int, k: int, m: int = 0) -> int:
@@ -210,6 +236,21 @@ def w12_lmhead_argmax(mat: W12Matrix, x, idx, max_logit, ws, stream=None):
 def w12_validate(mat: W12Matrix, ws: torch.Tensor, stream=None) -> int:
     d = mat.desc()
     return int(lib().w12_validate(ctypes.byref(d), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+PROBE_STATIC, PROBE_DYNAMIC, PROBE_STRIDE, PROBE_PIECES = 0, 1, 2, 3
+PROBE_WS_BYTES = 256
+
+
+def w12_probe_read(buf: torch.Tensor, nbytes: int, grid: int, block: int, loads: int, mode: int,
+                   stamps, ws: torch.Tensor, stream=None, lds_bytes: int = 0, piece: int = 0):
+    """Read-bandwidth probe (include/w12_probe.h) over the first `nbytes` of `buf`."""
+    if not buf.is_cuda or nbytes > buf.numel() * buf.element_size():
+        raise ValueError("probe buffer must be a device tensor holding nbytes")
+    if stamps is not None and (not stamps.is_cuda or stamps.numel() < 3 * grid or stamps.element_size() != 8):
+        raise ValueError("stamps must be a device tensor of 3 * grid 64-bit entries")
+    _check(lib().w12_probe_read(_ptr(buf), nbytes, grid, block, loads, mode, piece, lds_bytes, _ptr(stamps),
+                                _ptr(ws), ws.numel(), _stream(stream)), "w12_probe_read")
 
 
 # ---------------------------------------------------------------- conveniences

@@ -58,12 +58,6 @@ def download(mat: w12.W12Matrix):
     return rec, e_top, row_ptr, esc
 
 
-def strip_records(rec: np.ndarray, k: int, blocks) -> np.ndarray:
-    """Record bytes of the given 16-row blocks (block-major)."""
-    per = (k // 512) * 12288
-    r = rec.reshape(-1, per)
-    return r[np.asarray(blocks)].reshape(-1)
-
 
 def check_f32(y: np.ndarray, y64: np.ndarray, what: str):
     y = np.asarray(y, dtype=np.float64)
@@ -83,6 +77,18 @@ def check_bf16(y_bf16_bits: np.ndarray, y_f32: np.ndarray, y64: np.ndarray, what
     denom = np.maximum(np.abs(y64), FLOOR * s)
     err = np.abs(yb - y64) / np.where(denom > 0, denom, 1.0)
     assert float(err.max()) <= REL + BF16_ULP, f"{what}: BF16 error {float(err.max()):.3e}"
+
+
+def argmax_logits_f32(mat, x_dev):
+    """fp32 logits from the kernel the fused argmax runs (the helper-wave MFMA
+    kernel from 3 activation rows, the GEMV below), so that the argmax can be
+    compared with them bit for bit."""
+    m = x_dev.shape[0]
+    old = w12.set_tuning(w12.TUNE_PATH, w12.KERNEL_MFMA_HELPER if m >= 3 else 0)
+    try:
+        return w12.gemm(mat, x_dev, torch.float32)
+    finally:
+        w12.set_tuning(w12.TUNE_PATH, old)
 
 
 def gemm_both(mat, x_dev, q=False, apply_escapes=False):

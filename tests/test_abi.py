@@ -10,7 +10,8 @@ import pytest
 from lossless_compressed_weight_amd import w12
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "w12.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 # Fake, 256-byte aligned device addresses: argument checks must reject the
 # calls below before any HIP call could dereference them.
@@ -18,9 +19,11 @@ FAKE = 0x7F0000000000
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w \*]*?\b(w12_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*[A-Za-z_][\w \*]*?\b(w12_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -101,9 +104,13 @@ def test_workspace_sizes():
     assert w12.workspace_bytes(w12.OP_GEMM, 1024, 1024, 0) == 0            # bad M
     assert w12.workspace_bytes(99, 1024, 1024, 1) == 0
     for m in (1, 8, 15, 16, 32, 33, 64):
-        g = w12.workspace_bytes(w12.OP_GEMM, 17408, 5120, m)
-        a = w12.workspace_bytes(w12.OP_LMHEAD_ARGMAX, 17408, 5120, m)
-        assert g > 0 and a > g and g % 256 == 0
+        for op in (w12.OP_GEMM, w12.OP_GEMM_Q8, w12.OP_LMHEAD_ARGMAX):
+            b = w12.workspace_bytes(op, 17408, 5120, m)
+            assert b > 0 and b % 256 == 0
+            # whichever kernel the escape density selects, its plan fits
+            for n_esc in (0, 24000, 17408 * 100):
+                plan = w12.plan_info(_mat(17408, 5120, n_esc=n_esc), op, m)
+                assert plan["workspace_bytes"] <= b, (op, m, n_esc, plan)
     # the grid override changes the plan and therefore the size
     old = w12.set_tuning(w12.TUNE_GRID, 7)
     try:
@@ -118,3 +125,82 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(w12, "_lib", None)
     with pytest.raises(ImportError):
         w12.lib()
+
+
+def _plan_covers_rows(plan, n):
+    """Whole tiles and split tiles of a plan cover rows [0, n) exactly once."""
+    whole_rows = plan["grid"] * plan["whole_tiles"] * plan["tile_rows"]
+    split_rows = plan["split_tiles"] * plan["split_tile_rows"]
+    if plan["split_tiles"] == 0:
+        assert whole_rows >= n and whole_rows - n < plan["tile_rows"], plan
+    else:
+        assert whole_rows < n and whole_rows + split_rows >= n, plan
+        assert whole_rows + split_rows - n < plan["split_tile_rows"], plan
+    assert plan["split_units"] == plan["split_tiles"] * (plan["split_units"] // max(plan["split_tiles"], 1))
+    assert plan["split_tiles"] >= 0 and plan["split_units"] >= 0 and plan["whole_tiles"] >= 0
+
+
+@pytest.mark.parametrize("n,k,m", [
+    (12784, 5120, 32), (4112, 5120, 64), (16336, 4096, 8), (16336, 4096, 1),   # last whole tile cut short by N
+    (17408, 5120, 1), (17408, 5120, 32), (5120, 17408, 32), (1024, 5120, 64),
+    (151936, 5120, 16), (6144, 5120, 48), (16, 512, 3), (48, 1024, 40),
+])
+def test_plan_arithmetic(n, k, m):
+    """Host-side plan of every op: no negative split counts, every row covered
+    exactly once, a grid within [1, 4096] and no larger than the work units."""
+    for op in (w12.OP_GEMM, w12.OP_GEMM_Q8, w12.OP_LMHEAD_ARGMAX):
+        for n_esc in (0, n * 2, n * 50):
+            plan = w12.plan_info(_mat(n, k, n_esc=n_esc), op, m)
+            assert 1 <= plan["grid"] <= 4096
+            units = -(-n // plan["tile_rows"]) * (k // plan["unit_cols"])
+            assert plan["grid"] <= units
+            _plan_covers_rows(plan, n)
+            if op == w12.OP_LMHEAD_ARGMAX or (n_esc > 8 * n and op != w12.OP_GEMM_Q8):
+                assert plan["kernel"] in (w12.KERNEL_GEMV, w12.KERNEL_MFMA_HELPER)
+            if m <= 2:
+                assert plan["kernel"] == w12.KERNEL_GEMV
+
+
+def test_plan_of_whole_tiles_past_n_has_no_split_tiles():
+    """12784 x 5120 at M = 32: 799 row blocks in 200 tiles of 64 rows on 200
+    workgroups; the whole tiles already reach row 12800, so no rows are left
+    to split (a negative remainder once sent the kernel past N)."""
+    for path in (2, 3):
+        old = w12.set_tuning(w12.TUNE_PATH, path)
+        try:
+            plan = w12.plan_info(_mat(12784, 5120), w12.OP_GEMM, 32)
+        finally:
+            w12.set_tuning(w12.TUNE_PATH, old)
+        assert plan["split_tiles"] == 0 and plan["split_units"] == 0, plan
+        assert plan["grid"] * plan["whole_tiles"] * plan["tile_rows"] >= 12784
+
+
+def test_plan_info_argument_errors():
+    assert w12.lib().w12_plan_info(None, w12.OP_GEMM, 1, 0, None) == w12.E_INVALID_ARG
+    out = w12.PlanC()
+    lib = w12.lib()
+    assert lib.w12_plan_info(ctypes.byref(_mat(n=1000)), w12.OP_GEMM, 1, 0, ctypes.byref(out)) == \
+        w12.E_UNSUPPORTED_SHAPE
+    assert lib.w12_plan_info(ctypes.byref(_mat()), 99, 1, 0, ctypes.byref(out)) == w12.E_INVALID_ARG
+    assert lib.w12_plan_info(ctypes.byref(_mat()), w12.OP_GEMM, 65, 0, ctypes.byref(out)) == w12.E_M_RANGE
+    assert lib.w12_plan_info(ctypes.byref(_mat()), w12.OP_GEMM_Q8, 1, 8, ctypes.byref(out)) == w12.E_INVALID_ARG
+
+
+def test_tuning_hooks_are_per_thread():
+    """A tuning hook set on one thread leaves another thread's plans alone."""
+    import threading
+    base = w12.plan_info(_mat(17408, 5120), w12.OP_GEMM, 32)
+    seen = {}
+
+    def other():
+        seen["plan"] = w12.plan_info(_mat(17408, 5120), w12.OP_GEMM, 32)
+
+    old = w12.set_tuning(w12.TUNE_GRID, 7)
+    try:
+        assert w12.plan_info(_mat(17408, 5120), w12.OP_GEMM, 32)["grid"] == 7
+        th = threading.Thread(target=other)
+        th.start()
+        th.join()
+    finally:
+        w12.set_tuning(w12.TUNE_GRID, old)
+    assert seen["plan"] == base

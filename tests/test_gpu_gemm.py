@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import check_bf16, check_f32, dev16, gemm_both, host16, log, o, upload, w12
+from gpu_util import argmax_logits_f32, check_bf16, check_f32, dev16, gemm_both, host16, log, o, upload, w12
 
 pytestmark = pytest.mark.gpu
 
@@ -93,6 +93,25 @@ def test_default_grid_for_fewer_tiles_than_cus(n, k, m):
     w = synth.make_weights(n, k, synth.WORKLOADS[0], seed=n + k)
     log(f"[default grid] {n}x{k} M={m}")
     x = synth.make_activations(m, k, seed=31 + m)
+    mat = w12.encode(dev16(w))
+    yf, yb = gemm_both(mat, dev16(x))
+    y64 = o.gemm_ref(x, w)
+    check_f32(yf, y64, f"{n}x{k} M={m}")
+    check_bf16(yb, yf, y64, f"{n}x{k} M={m}")
+
+
+@pytest.mark.parametrize("n,k,m", [
+    (12784, 5120, 32),   # 200 tiles of 64 rows on 200 workgroups; the last tile has 48 rows
+    (4112, 5120, 64),    # 257 blocks in 129 tiles of 32 rows; the last tile has 16 rows
+    (16336, 4096, 8),    # 256 whole tiles on 256 workgroups; the last tile has 16 rows
+    (16336, 4096, 1),
+])
+def test_whole_tiles_reaching_past_n(n, k, m):
+    """Plans whose whole tiles already cover every row, with a last tile cut
+    short by N: no rows are left for split tiles, and every output matches."""
+    w = synth.make_weights(n, k, synth.WORKLOADS[0], seed=n + 3 * k)
+    log(f"[whole tiles past N] {n}x{k} M={m}")
+    x = synth.make_activations(m, k, seed=53 + m)
     mat = w12.encode(dev16(w))
     yf, yb = gemm_both(mat, dev16(x))
     y64 = o.gemm_ref(x, w)
@@ -237,7 +256,7 @@ def test_lmhead_argmax_small(m):
     x = synth.make_activations(m, w.shape[1], seed=500 + m)
     mat = w12.encode(dev16(w))
     idx, mx = w12.lmhead_argmax(mat, dev16(x))
-    yf = w12.gemm(mat, dev16(x), torch.float32).cpu().numpy()
+    yf = argmax_logits_f32(mat, dev16(x)).cpu().numpy()
     idx = idx.cpu().numpy()
     mx = mx.cpu().numpy()
     # the fused argmax is the argmax of the same kernel's fp32 logits
@@ -268,7 +287,7 @@ def test_lmhead_argmax_whole_tiles(m):
     log(f"[argmax whole tiles] {n}x{k} M={m}")
     mat = w12.encode(dev16(w))
     idx, mx = w12.lmhead_argmax(mat, dev16(x))
-    yf = w12.gemm(mat, dev16(x), torch.float32).cpu().numpy()
+    yf = argmax_logits_f32(mat, dev16(x)).cpu().numpy()
     idx = idx.cpu().numpy().astype(np.int64)
     assert np.array_equal(idx, np.argmax(yf, axis=1))
     assert np.array_equal(mx.cpu().numpy().view(np.uint32), yf[np.arange(m), idx].view(np.uint32))

@@ -23,7 +23,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import REL, check_bf16, check_f32, dev16, download, gemm_both, log, o, w12
+from gpu_util import REL, argmax_logits_f32, check_bf16, check_f32, dev16, download, gemm_both, log, o, w12
 
 pytestmark = pytest.mark.gpu
 
@@ -111,7 +111,7 @@ def test_lm_head_151936_argmax_full(lm_head, m):
     log(f"[lm head argmax] 151936x5120 M={m}")
     xd = dev16(x)
     idx, mx = w12.lmhead_argmax(mat, xd)
-    yf = w12.gemm(mat, xd, torch.float32).cpu().numpy()
+    yf = argmax_logits_f32(mat, xd).cpu().numpy()
     idx = idx.cpu().numpy().astype(np.int64)
     mx = mx.cpu().numpy()
     check_f32(yf, y64, f"lm head logits M={m}")
