@@ -35,19 +35,22 @@
 // End of a segment. Each wave leaves its MFMA accumulators in LDS; after a
 // barrier all 512 threads add the eight waves' sums in wave order and either
 // write the tile's outputs or, for a split tile, publish the values in the
-// workgroup's slot. Wave 0 stores the slot, makes it visible at agent scope
-// (release) and counts the workgroup into the tile's counter. The last
-// workgroup to arrive (acquire) adds all slots in workgroup order after its
-// own work is streamed and writes the tile; counters wrap back to zero.
+// workgroup's slot: every thread stores its values with agent-scope atomic
+// stores and waits until they have completed, then wave 0 counts the
+// workgroup into the tile's counter. The last workgroup to arrive adds all
+// slots (agent-scope atomic loads) in workgroup order after its own work is
+// streamed and writes the tile; counters wrap back to zero.
 #include "w12_internal.h"
 
 namespace w12 {
 namespace mx {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 8;                  // streaming waves per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kUnitCols = 512;
+constexpr int kUnitCols = 64 * kWaves;     // a unit: one 64-column chunk per wave
+constexpr int kWgPerCU = 8 / kWaves;       // workgroups per compute unit (eight waves per CU)
 constexpr int kCap = 256;  // escape substitutions one wave holds per segment
+constexpr int kRedRow = 65;  // floats per row of the reduction area (64 lanes + 1 of padding)
 
 template <int MT>
 constexpr int kRG = MT <= 2 ? 4 : 2;  // 16-row blocks of a whole tile
@@ -63,8 +66,8 @@ __device__ __forceinline__ uint32_t div_floor(uint64_t x, uint32_t y) {
   return q;
 }
 
-// First split unit of workgroup q (q in [0, P]); unit u is column unit u % kb
-// of split tile u / kb.
+// First split unit of workgroup q (q in [0, P]); unit u is column unit u % ku
+// of split tile u / ku.
 __device__ __forceinline__ uint32_t sk_start(const MxParams& a, int q) {
   return div_floor((uint64_t)q * (uint64_t)a.sk_units, (uint32_t)a.P);
 }
@@ -78,7 +81,7 @@ __device__ __forceinline__ int sk_owner(const MxParams& a, uint32_t u) {
 // if its second; -1 if q owns no unit of t.
 __device__ __forceinline__ int part_slot(const MxParams& a, int q, int t) {
   const uint32_t s = sk_start(a, q), e = sk_start(a, q + 1);
-  const uint32_t t0 = (uint32_t)t * (uint32_t)a.kb, t1 = t0 + (uint32_t)a.kb;
+  const uint32_t t0 = (uint32_t)t * (uint32_t)a.ku, t1 = t0 + (uint32_t)a.ku;
   if (s >= e || e <= t0 || s >= t1) return -1;
   return 2 * q + ((s >= t0) ? 0 : 1);
 }
@@ -113,9 +116,9 @@ __device__ __forceinline__ SegList seg_list(const MxParams& a, int p) {
   L.sk0 = L.sk1 = Seg{0, 0, 0, 0, -1, -1};
   const uint32_t s0 = sk_start(a, p), s1 = sk_start(a, p + 1);
   if (s1 > s0) {
-    const int ta = (int)div_floor(s0, (uint32_t)a.kb), tz = (int)div_floor(s1 - 1, (uint32_t)a.kb);
-    const uint32_t ua = (uint32_t)ta * (uint32_t)a.kb, uz = (uint32_t)tz * (uint32_t)a.kb;
-    const Seg A = split_seg<TB>(a, ta, (int)(s0 - ua), ta == tz ? (int)(s1 - ua) : a.kb, 0);
+    const int ta = (int)div_floor(s0, (uint32_t)a.ku), tz = (int)div_floor(s1 - 1, (uint32_t)a.ku);
+    const uint32_t ua = (uint32_t)ta * (uint32_t)a.ku, uz = (uint32_t)tz * (uint32_t)a.ku;
+    const Seg A = split_seg<TB>(a, ta, (int)(s0 - ua), ta == tz ? (int)(s1 - ua) : a.ku, 0);
     if (ta == tz) {
       L.nsk = 1;
       L.sk0 = A;
@@ -135,19 +138,19 @@ template <int GB>
 __device__ __forceinline__ Seg seg_at(const MxParams& a, const SegList& L, int i) {
   if (i < L.nsk) return i == 0 ? L.sk0 : L.sk1;
   const int r0 = (L.dp0 + i - L.nsk) * GB * 16;
-  return Seg{r0, min(GB, (a.n - r0) >> 4), 0, a.kb, -1, -1};
+  return Seg{r0, min(GB, (a.n - r0) >> 4), 0, a.ku, -1, -1};
 }
 
 // -------------------------------------------------------------- LDS
 template <int MT>
 struct Lds {
-  // each wave's MFMA accumulators of the current segment: [block][m-tile][element][lane]
-  float red[kWaves][kRG<MT>][MT][4][64];
-  // a split segment's finished values [activation row][row], which wave 0 publishes
-  float fin[16 * MT][kRG<MT> * 16];
-  // per wave: the segment's escape substitutions {packed target and bits, unit}
+  // each wave's MFMA accumulators of the current segment: [block][m-tile][element][lane],
+  // rows padded to 65 floats so that the reduction's reads (64 output rows of
+  // one activation row) spread over the banks
+  float red[kWaves][kRG<MT>][MT][4][kRedRow];
+  // per wave: the segment's escape substitutions {packed target and bits,
+  // unit}, their count, and the row pointers of the segment's rows
   uint2 list[kWaves][kCap];
-  // per wave: row pointers of the segment's rows
   uint32_t rp[kWaves][65];
   int last[2];  // split tiles this workgroup finishes last: tile + 1, or 0
 };
@@ -201,17 +204,30 @@ __device__ __forceinline__ int entry_row(const uint32_t* rp, int R, uint32_t idx
   return lo;
 }
 
-constexpr int kEscBatch = 4;  // entry loads per lane in flight while building a list
+constexpr int kEscBatch = 8;  // entry loads per lane in flight while building a list (512 entries)
 
 // The wave's escapes of segment s (rows row0 .. row0 + R - 1, units [k0, k1),
 // 64-column chunk `wave` of each unit), in CSR order: the first kCap go to the
 // LDS list; returns how many there are.
+// The first batch of a segment's escape entries, [e0, e0 + 64 kEscBatch).
+__device__ __forceinline__ void load_entries(const MxParams& a, uint32_t b, uint32_t e1, int lane,
+                                             uint2 (&ev)[kEscBatch]) {
+#pragma unroll
+  for (int k = 0; k < kEscBatch; ++k) {
+    const uint32_t idx = b + 64 * k + lane;
+    ev[k] = idx < e1 ? a.esc[idx] : make_uint2(0xFFFFFFFFu, 0u);
+  }
+}
+
+// r_lane and e1 are the row pointers of row row0 + lane and of row row0 + R,
+// ev the first batch of entries; the caller loads both ahead of the
+// segment's first weight loads (the entries after the row pointers arrive),
+// so neither round trip queues behind the weight stream.
 template <int MT>
-__device__ __forceinline__ int build_list(const MxParams& a, Lds<MT>& sh, const Seg& s, int wave, int lane) {
+__device__ __forceinline__ int build_list(const MxParams& a, Lds<MT>& sh, const Seg& s, int wave, int lane,
+                                          uint32_t r_lane, uint32_t e1, const uint2 (&ev0)[kEscBatch]) {
   const int R = s.rg * 16;
   uint32_t* rp = sh.rp[wave];
-  const uint32_t r_lane = a.row_ptr[s.row0 + min(lane, R)];
-  const uint32_t e1 = a.row_ptr[s.row0 + R];
   if (lane < R) rp[lane] = r_lane;
   if (lane == 0) rp[R] = e1;
   __builtin_amdgcn_wave_barrier();
@@ -219,16 +235,17 @@ __device__ __forceinline__ int build_list(const MxParams& a, Lds<MT>& sh, const 
   int cnt = 0;
   for (uint32_t b = e0; b < e1; b += 64 * kEscBatch) {
     uint2 ev[kEscBatch];
+    if (b == e0) {
 #pragma unroll
-    for (int k = 0; k < kEscBatch; ++k) {
-      const uint32_t idx = b + 64 * k + lane;
-      ev[k] = idx < e1 ? a.esc[idx] : make_uint2(0xFFFFFFFFu, 0u);
+      for (int k = 0; k < kEscBatch; ++k) ev[k] = ev0[k];
+    } else {
+      load_entries(a, b, e1, lane, ev);
     }
 #pragma unroll
     for (int k = 0; k < kEscBatch; ++k) {
       const uint32_t idx = b + 64 * k + lane;
-      const uint32_t col = ev[k].x, u = col >> 9;
-      const bool keep = idx < e1 && u >= (uint32_t)s.k0 && u < (uint32_t)s.k1 && ((col >> 6) & 7u) == (uint32_t)wave;
+      const uint32_t col = ev[k].x, u = col / kUnitCols;
+      const bool keep = idx < e1 && u >= (uint32_t)s.k0 && u < (uint32_t)s.k1 && (col >> 6) % kWaves == (uint32_t)wave;
       const uint64_t bal = __ballot(keep);
       if (keep) {
         const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
@@ -257,8 +274,8 @@ __device__ __forceinline__ void overflow_fix(const MxParams& a, Lds<MT>& sh, con
   for (uint32_t b = e0; b < e1; b += 64) {
     const uint32_t idx = b + lane;
     const uint2 ev = idx < e1 ? a.esc[idx] : make_uint2(0xFFFFFFFFu, 0u);
-    const uint32_t col = ev.x, u = col >> 9;
-    const bool keep = idx < e1 && u >= (uint32_t)s.k0 && u < (uint32_t)s.k1 && ((col >> 6) & 7u) == (uint32_t)wave;
+    const uint32_t col = ev.x, u = col / kUnitCols;
+    const bool keep = idx < e1 && u >= (uint32_t)s.k0 && u < (uint32_t)s.k1 && (col >> 6) % kWaves == (uint32_t)wave;
     uint64_t bal = __ballot(keep);
     const int nk = __popcll(bal);
     // the first kCap kept entries were substituted in the stream
@@ -313,8 +330,7 @@ __device__ __forceinline__ int seg_stream(const MxParams& a, Lds<MT>& sh, const 
   }
   const uint8_t* blk = a.rec + (int64_t)(s.row0 >> 4) * a.kb * kRecBytes;
   const uint32_t blk_stride = (uint32_t)a.kb * kRecBytes;
-  const uint32_t voff = (uint32_t)wave * 1024u + (uint32_t)lane * 16u;
-  const uint32_t boff = kViewBytes + (uint32_t)wave * 512u + (uint32_t)lane * 8u;
+  const uint32_t voff = (uint32_t)lane * 16u, boff = kViewBytes + (uint32_t)lane * 8u;
   const uint16_t* xr[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -327,11 +343,14 @@ __device__ __forceinline__ int seg_stream(const MxParams& a, Lds<MT>& sh, const 
       st.x[mt][0] = *reinterpret_cast<const uint4*>(xr[mt] + (int64_t)u * kUnitCols);
       st.x[mt][1] = *reinterpret_cast<const uint4*>(xr[mt] + (int64_t)u * kUnitCols + 8);
     }
+    // this wave's 64-column chunk c of the row: record c / 8, chunk c % 8 in it
+    const uint32_t c = (uint32_t)u * kWaves + (uint32_t)wave;
+    const uint32_t rec_off = (c >> 3) * kRecBytes;
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
-      const uint32_t o = (uint32_t)j * blk_stride + (uint32_t)u * kRecBytes;
-      st.v[j] = load_stream16(blk + (o + voff));
-      if (!Q) st.b[j] = load_stream8(blk + (o + boff));
+      const uint32_t o = (uint32_t)j * blk_stride + rec_off;
+      st.v[j] = load_stream16(blk + (o + (c & 7) * 1024u + voff));
+      if (!Q) st.b[j] = load_stream8(blk + (o + (c & 7) * 512u + boff));
     }
   };
   f32x4_t acc[RG][MT];
@@ -373,11 +392,21 @@ __device__ __forceinline__ int seg_stream(const MxParams& a, Lds<MT>& sh, const 
   // loop, unit i + 2 loads while unit i + 1's data arrive and unit i computes.
   const int u0 = s.k0, n = s.k1 - s.k0;
   int cnt = 0;
+  // The escape list's round trips (row pointers, then the first batch of
+  // entries) go out ahead of the segment's weight loads, so they do not queue
+  // behind them; the list is built while the first two units load.
+  uint32_t r_lane = 0u, e1 = 0u;
+  uint2 ev0[kEscBatch];
+  if (a.fix) {
+    r_lane = a.row_ptr[s.row0 + min(lane, s.rg * 16)];
+    e1 = a.row_ptr[s.row0 + s.rg * 16];
+    load_entries(a, __builtin_amdgcn_readfirstlane(r_lane), e1, lane, ev0);
+  }
   Stage<MT, RG, Q> sa, sb;
   load(sa, u0);
   if (n > 1) load(sb, u0 + 1);
   if (a.fix) {
-    cnt = build_list<MT>(a, sh, s, wave, lane);
+    cnt = build_list<MT>(a, sh, s, wave, lane, r_lane, e1, ev0);
     ne = min(cnt, kCap);
   }
   if (n == 1) {
@@ -444,9 +473,9 @@ __device__ __forceinline__ void wave_sums(const Lds<MT>& sh, int r, int m0, floa
 // Workgroups that hold units of split tile t, and how many of them there are
 // (wave-uniform; every lane of the calling wave active).
 __device__ __forceinline__ int tile_sharers(const MxParams& a, int t, int& pa, int& pb, int lane) {
-  const uint32_t u_first = (uint32_t)t * (uint32_t)a.kb;
+  const uint32_t u_first = (uint32_t)t * (uint32_t)a.ku;
   pa = sk_owner(a, u_first);
-  pb = sk_owner(a, u_first + (uint32_t)a.kb - 1);
+  pb = sk_owner(a, u_first + (uint32_t)a.ku - 1);
   int cnt = 0;
   for (int q0 = pa; q0 <= pb; q0 += 64) {
     const int q = q0 + lane;
@@ -457,7 +486,7 @@ __device__ __forceinline__ int tile_sharers(const MxParams& a, int t, int& pa, i
 
 // ============================================================== kernel
 template <int MT, bool Q, int TB>
-__global__ __launch_bounds__(kThreads, 1) void k_mx(MxParams a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_mx(MxParams a) {
   constexpr int RG = kRG<MT>;
   constexpr int MM = 16 * MT;
   constexpr int ROWS = RG * 16;       // rows of a whole tile
@@ -498,25 +527,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx(MxParams a) {
       __syncthreads();  // sh.red is free for the next segment
       continue;
     }
-    // split tile: finished values to LDS; wave 0 publishes them
-    if (r < TS) {
+    // split tile: every thread stores its values in the workgroup's slot with
+    // agent-scope atomic stores, which complete at the device's coherence
+    // point; each wave waits for its stores, and once all have (barrier),
+    // wave 0 counts the workgroup in. (Release and acquire fences at agent
+    // scope would write back and invalidate the whole L2 of the XCD, which
+    // under the weight stream took 10-30 us.)
+    {
+      float* slot = a.part + (int64_t)(2 * p + s.part) * MM * TS;
+      if (r < TS) {
 #pragma unroll
-      for (int q = 0; q < J; ++q)
-        if (m0 + MS * q < MM) sh.fin[m0 + MS * q][r] = v[q];
+        for (int q = 0; q < J; ++q) {
+          const int m = m0 + MS * q;
+          if (m < a.m) __hip_atomic_store(&slot[m * TS + r], v[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
     if (wave == 0) {
-      float* slot = a.part + (int64_t)(2 * p + s.part) * MM * TS;
-      for (int q = lane; q < a.m * TS; q += 64)
-        __hip_atomic_store(&slot[q], sh.fin[q / TS][q % TS], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       int pa, pb;
       const int cnt = tile_sharers(a, s.tile, pa, pb, lane);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the slot is visible before the count
       // The owner of a split tile's first unit owns no other tile's first
       // unit (a workgroup's split units span at most one tile's length), so
       // its index names the tile's counter.
       uint32_t old = 0u;
-      if (lane == 0) old = __builtin_amdgcn_atomic_inc32(&a.ctr[pa], (uint32_t)cnt - 1u, __ATOMIC_ACQ_REL, "agent");
+      if (lane == 0) old = __builtin_amdgcn_atomic_inc32(&a.ctr[pa], (uint32_t)cnt - 1u, __ATOMIC_RELAXED, "agent");
       if (np == 0) t0 = s.tile, pa0 = pa, pb0 = pb, c0 = cnt, old0 = old;
       else t1 = s.tile, pa1 = pa, pb1 = pb, c1 = cnt, old1 = old;
     }
@@ -568,22 +604,23 @@ MxPlan plan_mx(int64_t n, int64_t k, int64_t m, int64_t grid_override) {
   MxPlan pl{};
   const int64_t mt = (m + 15) / 16;
   pl.gb = mt <= 2 ? 4 : 2;
-  const int64_t kb = k / kRecCols;
+  const int64_t kb = k / mx::kUnitCols;  // units per row
   const int64_t nb = n / 16;
   const int64_t tiles = (nb + pl.gb - 1) / pl.gb;
-  // One workgroup (eight waves) per compute unit; with fewer tiles than CUs,
-  // c equal sharers per tile (c * T workgroups), or whole tiles on T
-  // workgroups when the idle CUs cost little.
-  int64_t P = kNumCU;
+  // Eight streaming waves per compute unit (kWgPerCU workgroups); with fewer
+  // tiles than workgroup slots, c equal sharers per tile (c * T workgroups),
+  // or whole tiles on T workgroups when the idle slots cost little.
+  const int64_t slots = (int64_t)kNumCU * mx::kWgPerCU;
+  int64_t P = slots;
   if (grid_override > 0) {
     P = grid_override;
-  } else if (tiles < kNumCU) {
-    const int64_t c = kNumCU / tiles;
+  } else if (tiles < slots) {
+    const int64_t c = slots / tiles;
     if (c >= 2) {
       P = c * tiles;
     } else {
       const int64_t tile_bytes = pl.gb * 16 * k * 3 / 2;
-      if (tile_bytes * (kNumCU - tiles) <= kWholeTileSlack * kNumCU) P = tiles;
+      if (tile_bytes * (slots - tiles) <= kWholeTileSlack * slots) P = tiles;
     }
   }
   if (P > kMaxGrid) P = kMaxGrid;
@@ -600,6 +637,8 @@ MxPlan plan_mx(int64_t n, int64_t k, int64_t m, int64_t grid_override) {
   pl.sk_tiles = (int)((rem + pl.tb - 1) / pl.tb);
   pl.sk_units = (int64_t)pl.sk_tiles * kb;
   pl.part_bytes = (size_t)(2 * P) * (size_t)(mt * 16) * (size_t)(pl.tb * 16) * sizeof(float);
+  pl.threads = mx::kThreads;
+  pl.unit_cols = mx::kUnitCols;
   return pl;
 }
 
@@ -621,6 +660,7 @@ static hipError_t launch_mx_q(const MxPlan& pl, const MxParams& p, hipStream_t s
 }
 
 hipError_t launch_mx(const MxPlan& pl, MxParams p, hipStream_t s) {
+  p.ku = p.k / mx::kUnitCols;
   p.P = pl.P;
   p.dp = pl.dp;
   p.sk_row0 = pl.sk_row0;

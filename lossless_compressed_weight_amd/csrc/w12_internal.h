@@ -223,10 +223,11 @@ struct MxParams {
   int64_t ldy;
   uint32_t* ctr;             // split-tile counters [sk_tiles]; zero between calls
   float* part;               // split slots [2P][MM][tile_rows]
-  int64_t sk_units;          // 512-column units of the split tiles
+  int64_t sk_units;          // units of the split tiles
   int sk_row0;               // first row of the split tiles
   int n, k;
-  int kb;                    // records (and units) per 16-row block: K / 512
+  int kb;                    // records per 16-row block: K / 512
+  int ku;                    // stream-K units per 16-row block: K / unit width
   int P;                     // workgroups
   int dp;                    // whole tiles per workgroup
   int m;                     // activation rows
@@ -244,6 +245,8 @@ struct MxPlan {
   int sk_tiles;
   int64_t sk_units;
   size_t part_bytes;
+  int threads;    // threads per workgroup
+  int unit_cols;  // columns of a stream-K unit
 };
 // Largest K the stream kernel takes (its per-segment unit count fits the
 // escape bucket arithmetic); larger K runs the helper-wave kernel.

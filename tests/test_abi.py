@@ -159,20 +159,26 @@ def test_plan_arithmetic(n, k, m):
                 assert plan["kernel"] in (w12.KERNEL_GEMV, w12.KERNEL_MFMA_HELPER)
             if m <= 2:
                 assert plan["kernel"] == w12.KERNEL_GEMV
+            elif -(-(n // 16) // 4) < 256 and m <= 32 and op != w12.OP_LMHEAD_ARGMAX and (n_esc <= 8 * n or op == w12.OP_GEMM_Q8):
+                assert plan["kernel"] == w12.KERNEL_MFMA_STREAM and plan["prepass"] == 0
+            else:
+                assert plan["kernel"] == w12.KERNEL_MFMA_HELPER
 
 
-def test_plan_of_whole_tiles_past_n_has_no_split_tiles():
-    """12784 x 5120 at M = 32: 799 row blocks in 200 tiles of 64 rows on 200
-    workgroups; the whole tiles already reach row 12800, so no rows are left
-    to split (a negative remainder once sent the kernel past N)."""
-    for path in (2, 3):
-        old = w12.set_tuning(w12.TUNE_PATH, path)
-        try:
-            plan = w12.plan_info(_mat(12784, 5120), w12.OP_GEMM, 32)
-        finally:
-            w12.set_tuning(w12.TUNE_PATH, old)
-        assert plan["split_tiles"] == 0 and plan["split_units"] == 0, plan
-        assert plan["grid"] * plan["whole_tiles"] * plan["tile_rows"] >= 12784
+@pytest.mark.parametrize("path,n,k", [
+    (2, 12784, 5120),   # helper-wave kernel: 799 row blocks in 200 tiles on 200 workgroups
+    (3, 16368, 1024),   # stream kernel: 1023 row blocks in 256 tiles on 256 workgroups
+])
+def test_plan_of_whole_tiles_past_n_has_no_split_tiles(path, n, k):
+    """Whole tiles that already reach past N (the last one cut short) leave no
+    rows to split (a negative remainder once sent the kernel past N)."""
+    old = w12.set_tuning(w12.TUNE_PATH, path)
+    try:
+        plan = w12.plan_info(_mat(n, k), w12.OP_GEMM, 32)
+    finally:
+        w12.set_tuning(w12.TUNE_PATH, old)
+    assert plan["whole_tiles"] == 1 and plan["split_tiles"] == 0 and plan["split_units"] == 0, plan
+    assert plan["grid"] * plan["whole_tiles"] * plan["tile_rows"] >= n
 
 
 def test_plan_info_argument_errors():

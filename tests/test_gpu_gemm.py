@@ -102,15 +102,19 @@ def test_default_grid_for_fewer_tiles_than_cus(n, k, m):
 
 @pytest.mark.parametrize("n,k,m", [
     (12784, 5120, 32),   # 200 tiles of 64 rows on 200 workgroups; the last tile has 48 rows
+    (16368, 1024, 32),   # 256 tiles on 256 workgroups; the last tile has 48 rows
     (4112, 5120, 64),    # 257 blocks in 129 tiles of 32 rows; the last tile has 16 rows
     (16336, 4096, 8),    # 256 whole tiles on 256 workgroups; the last tile has 16 rows
     (16336, 4096, 1),
 ])
-def test_whole_tiles_reaching_past_n(n, k, m):
+@pytest.mark.parametrize("path", [0, 3])
+def test_whole_tiles_reaching_past_n(n, k, m, path):
     """Plans whose whole tiles already cover every row, with a last tile cut
-    short by N: no rows are left for split tiles, and every output matches."""
+    short by N: no rows are left for split tiles, and every output matches
+    (the library's kernel choice, and the stream kernel forced)."""
+    w12.set_tuning(w12.TUNE_PATH, path)
     w = synth.make_weights(n, k, synth.WORKLOADS[0], seed=n + 3 * k)
-    log(f"[whole tiles past N] {n}x{k} M={m}")
+    log(f"[whole tiles past N] {n}x{k} M={m} path={path}")
     x = synth.make_activations(m, k, seed=53 + m)
     mat = w12.encode(dev16(w))
     yf, yb = gemm_both(mat, dev16(x))
