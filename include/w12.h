@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define W12_ABI_VERSION 1
+#define W12_ABI_VERSION 2
 #define W12_FORMAT_VERSION 1
 
 #define W12_REC_ROWS 16
@@ -144,10 +144,14 @@ int w12_encode_plan(const uint16_t* w, int64_t n, int64_t k, uint8_t* e_top, uin
 
 /* Encode, step 2 (section 4.1 and Figure 5: split into planes, pack records,
  * list escapes). Inputs w, e_top, esc_row_ptr as produced by w12_encode_plan;
- * outputs records ((N/16)*(K/512)*12288 bytes, 16-byte aligned) and esc
- * (esc_row_ptr[N] entries; may be NULL if that is 0). */
+ * outputs records ((N/16)*(K/512)*12288 bytes, 16-byte aligned) and esc, a
+ * buffer of esc_capacity entries (pass the count w12_encode_plan returned;
+ * esc may be NULL only when esc_capacity is 0). Entries past esc_capacity are
+ * never written: a smaller capacity than the count truncates the list.
+ * W12_E_INVALID_ARG for a negative capacity, one above N*K, or a NULL esc
+ * with a nonzero capacity. */
 int w12_encode(const uint16_t* w, int64_t n, int64_t k, const uint8_t* e_top, const uint32_t* esc_row_ptr,
-               uint8_t* records, w12_escape* esc, void* stream);
+               uint8_t* records, w12_escape* esc, int64_t esc_capacity, void* stream);
 
 /* Exact decode (section 4.1: the load-time bit-for-bit check): writes the
  * original BF16 matrix [N, K] (row-major, 16-byte aligned) to w_out. */

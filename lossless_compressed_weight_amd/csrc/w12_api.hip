@@ -299,11 +299,12 @@ int w12_encode_plan(const uint16_t* w, int64_t n, int64_t k, uint8_t* e_top, uin
 }
 
 int w12_encode(const uint16_t* w, int64_t n, int64_t k, const uint8_t* e_top, const uint32_t* esc_row_ptr,
-               uint8_t* records, w12_escape* esc, void* stream) {
+               uint8_t* records, w12_escape* esc, int64_t esc_capacity, void* stream) {
   const int s = check_shape(n, k);
   if (s != W12_OK) return s;
   if (!w || !e_top || !esc_row_ptr || !records || !aligned16(w) || !aligned16(records)) return W12_E_INVALID_ARG;
-  const hipError_t e = launch_pack(w, (int)n, (int)k, e_top, esc_row_ptr, records, esc,
+  if (esc_capacity < 0 || esc_capacity > n * k || (esc_capacity > 0 && !esc)) return W12_E_INVALID_ARG;
+  const hipError_t e = launch_pack(w, (int)n, (int)k, e_top, esc_row_ptr, records, esc, (uint32_t)esc_capacity,
                                    reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "encode: pack kernel");
   return W12_OK;

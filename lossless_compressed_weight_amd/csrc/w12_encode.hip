@@ -93,7 +93,8 @@ __global__ __launch_bounds__(1024) void k_scan(const uint32_t* __restrict__ cnt,
 __global__ __launch_bounds__(1024) void k_pack(const uint16_t* __restrict__ w, int n, int k,
                                                const uint8_t* __restrict__ e_top,
                                                const uint32_t* __restrict__ row_ptr,
-                                               uint8_t* __restrict__ rec, w12_escape* __restrict__ esc) {
+                                               uint8_t* __restrict__ rec, w12_escape* __restrict__ esc,
+                                               uint32_t esc_cap) {
   const int lane = threadIdx.x & 63;
   const int r = threadIdx.x >> 6;
   const int rb = blockIdx.x;
@@ -149,7 +150,8 @@ __global__ __launch_bounds__(1024) void k_pack(const uint16_t* __restrict__ w, i
         ev.col = (uint32_t)(kb * kRecCols + lane * 8 + j);
         ev.bits = (uint16_t)bits;
         ev.ph = (uint16_t)ph[j];
-        esc[pos++] = ev;
+        if (pos < esc_cap) esc[pos] = ev;  // never past the caller's buffer
+        ++pos;
       }
     }
     out_pos += total;
@@ -240,8 +242,8 @@ hipError_t launch_scan(const uint32_t* cnt, int n, uint32_t* row_ptr, hipStream_
 }
 
 hipError_t launch_pack(const uint16_t* w, int n, int k, const uint8_t* e_top, const uint32_t* row_ptr,
-                       uint8_t* rec, w12_escape* esc, hipStream_t s) {
-  hipLaunchKernelGGL(k_pack, dim3(n / kRecRows), dim3(1024), 0, s, w, n, k, e_top, row_ptr, rec, esc);
+                       uint8_t* rec, w12_escape* esc, uint32_t esc_cap, hipStream_t s) {
+  hipLaunchKernelGGL(k_pack, dim3(n / kRecRows), dim3(1024), 0, s, w, n, k, e_top, row_ptr, rec, esc, esc_cap);
   return hipGetLastError();
 }
 

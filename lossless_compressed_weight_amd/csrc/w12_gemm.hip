@@ -1127,7 +1127,7 @@ __device__ __forceinline__ void helper(const GemmParams& a, HelperLds<MM, ROWS>&
   publish(-1);
 }
 
-// ============================================================== GEMV (M < 16)
+// ============================================================== GEMV (lane per row; chosen for M <= 2)
 // A streaming wave covers 64 rows (lane = row, four 16-row blocks) and one
 // 16-column group per step: each lane loads the 16 view bytes and 8 B-plane
 // bytes of its own row, rebuilds 16 weights and accumulates M dot products.
@@ -1226,7 +1226,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t*
   final_share<M, kGemvTileRows, kGemvTileRows>(a, sh.h, L, lane, wave);
 }
 
-// ============================================================== MFMA (M >= 16)
+// ============================================================== MFMA with helper waves (chosen from M = 3)
 // v_mfma_f32_16x16x32_bf16 with A = 16 weight rows x 32 columns decoded in
 // registers and B = 32 columns x 16 activation rows loaded straight from
 // global memory. A wave's 1 KB view load of one 64-column chunk of a 16-row

@@ -183,7 +183,7 @@ enum { kModeStore = 0, kModeArgmax = 1 };
 hipError_t launch_plan(const uint16_t* w, int n, int k, uint8_t* e_top, uint32_t* cnt, hipStream_t s);
 hipError_t launch_scan(const uint32_t* cnt, int n, uint32_t* row_ptr, hipStream_t s);
 hipError_t launch_pack(const uint16_t* w, int n, int k, const uint8_t* e_top, const uint32_t* row_ptr,
-                       uint8_t* rec, w12_escape* esc, hipStream_t s);
+                       uint8_t* rec, w12_escape* esc, uint32_t esc_cap, hipStream_t s);
 hipError_t launch_decode(const w12_matrix* m, uint16_t* out, hipStream_t s);
 hipError_t launch_validate(const w12_matrix* m, uint32_t* flag, hipStream_t s);
 

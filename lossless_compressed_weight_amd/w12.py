@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw12.so")
 
 # constants mirrored from include/w12.h
-ABI_VERSION = 1
+ABI_VERSION = 2
 FORMAT_VERSION = 1
 REC_ROWS, REC_COLS, REC_BYTES, REC_VIEW_BYTES = 16, 512, 12288, 8192
 MAX_M = 64
@@ -71,7 +71,7 @@ _SIGNATURES = {
     "w12_last_error": (ctypes.c_char_p, []),
     "w12_workspace_bytes": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
     "w12_encode_plan": (ctypes.c_int, [_P, _I64, _I64, _P, _P, ctypes.POINTER(_I64), _P, _SZ, _P]),
-    "w12_encode": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "w12_encode": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _I64, _P]),
     "w12_decode": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _P]),
     "w12_gemm": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _SZ, _P]),
     "w12_gemm_q8": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _I64, ctypes.c_int,
@@ -191,6 +191,37 @@ def _as_bits16(t: torch.Tensor) -> torch.Tensor:
     raise TypeError(f"expected BF16 data (bfloat16, int16 or uint16 tensor), got {t.dtype}")
 
 
+def _on(mat: "W12Matrix", t: torch.Tensor, what: str):
+    if not t.is_cuda or t.device != mat.device:
+        raise ValueError(f"{what} must live on the matrix's device {mat.device}, got {t.device}")
+
+
+def _check_x(mat: "W12Matrix", x: torch.Tensor):
+    """Activations: BF16 bits, [M, K] with unit column stride, on mat's device."""
+    _as_bits16(x)
+    _on(mat, x, "x")
+    if x.dim() != 2 or x.shape[1] != mat.k or (x.shape[0] > 0 and x.stride(1) != 1):
+        raise ValueError(f"x must be [M, {mat.k}] with unit column stride, got {tuple(x.shape)} "
+                         f"strides {tuple(x.stride())}")
+
+
+def _check_y(mat: "W12Matrix", y: torch.Tensor, m: int) -> int:
+    """Output: float32 or bfloat16 [M, N] with unit column stride; returns its dtype code."""
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"y must be float32 or bfloat16, got {y.dtype}")
+    _on(mat, y, "y")
+    if y.dim() != 2 or tuple(y.shape) != (m, mat.n) or (m > 0 and y.stride(1) != 1):
+        raise ValueError(f"y must be [{m}, {mat.n}] with unit column stride, got {tuple(y.shape)} "
+                         f"strides {tuple(y.stride())}")
+    return F32 if y.dtype == torch.float32 else BF16
+
+
+def _check_ws(mat: "W12Matrix", ws: torch.Tensor):
+    _on(mat, ws, "workspace")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+
+
 # ---------------------------------------------------------------- C-named calls
 def w12_encode_plan(w: torch.Tensor, e_top: torch.Tensor, row_ptr: torch.Tensor, ws: torch.Tensor,
                     stream=None) -> int:
@@ -201,39 +232,61 @@ def w12_encode_plan(w: torch.Tensor, e_top: torch.Tensor, row_ptr: torch.Tensor,
     return int(n_esc.value)
 
 
-def w12_encode(w, e_top, row_ptr, records, esc, stream=None):
+def w12_encode(w, e_top, row_ptr, records, esc, stream=None, n_esc=None):
+    """esc: int64 device tensor of at least n_esc entries (n_esc: the count
+    w12_encode_plan returned; default: all of esc), or None when it is 0."""
     n, k = w.shape
+    cap = 0 if esc is None else (esc.numel() if n_esc is None else n_esc)
+    if esc is not None and (esc.dtype != torch.int64 or not esc.is_cuda or esc.numel() < cap):
+        raise ValueError("esc must be an int64 device tensor with room for the escape entries")
     _check(lib().w12_encode(_ptr(w), n, k, _ptr(e_top), _ptr(row_ptr), _ptr(records),
-                            _ptr(esc) if esc is not None and esc.numel() else ctypes.c_void_p(0),
-                            _stream(stream)), "w12_encode")
+                            _ptr(esc) if cap else ctypes.c_void_p(0), cap, _stream(stream)), "w12_encode")
 
 
 def w12_decode(mat: W12Matrix, out: torch.Tensor, stream=None):
+    _on(mat, out, "out")
+    if out.element_size() != 2 or not out.is_contiguous() or out.numel() != mat.n * mat.k:
+        raise ValueError(f"out must be a contiguous 16-bit tensor of {mat.n} x {mat.k} elements")
     d = mat.desc()
     _check(lib().w12_decode(ctypes.byref(d), _ptr(out), _stream(stream)), "w12_decode")
 
 
 def w12_gemm(mat: W12Matrix, x, y, ws, stream=None):
+    _check_x(mat, x)
+    ydt = _check_y(mat, y, x.shape[0])
+    _check_ws(mat, ws)
     d = mat.desc()
-    ydt = F32 if y.dtype == torch.float32 else BF16
     _check(lib().w12_gemm(ctypes.byref(d), _ptr(x), x.shape[0], x.stride(0), _ptr(y), y.stride(0), ydt,
                           _ptr(ws), ws.numel(), _stream(stream)), "w12_gemm")
 
 
 def w12_gemm_q8(mat: W12Matrix, x, y, flags, ws, stream=None):
+    _check_x(mat, x)
+    ydt = _check_y(mat, y, x.shape[0])
+    _check_ws(mat, ws)
     d = mat.desc()
-    ydt = F32 if y.dtype == torch.float32 else BF16
     _check(lib().w12_gemm_q8(ctypes.byref(d), _ptr(x), x.shape[0], x.stride(0), _ptr(y), y.stride(0), ydt,
                              flags, _ptr(ws), ws.numel(), _stream(stream)), "w12_gemm_q8")
 
 
 def w12_lmhead_argmax(mat: W12Matrix, x, idx, max_logit, ws, stream=None):
+    _check_x(mat, x)
+    m = x.shape[0]
+    _on(mat, idx, "idx")
+    if idx.dtype != torch.int32 or idx.numel() < m or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 tensor of M entries")
+    if max_logit is not None:       # optional: NULL skips the maximum logits
+        _on(mat, max_logit, "max_logit")
+        if max_logit.dtype != torch.float32 or max_logit.numel() < m or not max_logit.is_contiguous():
+            raise ValueError("max_logit must be a contiguous float32 tensor of M entries")
+    _check_ws(mat, ws)
     d = mat.desc()
     _check(lib().w12_lmhead_argmax(ctypes.byref(d), _ptr(x), x.shape[0], x.stride(0), _ptr(idx), _ptr(max_logit),
                                    _ptr(ws), ws.numel(), _stream(stream)), "w12_lmhead_argmax")
 
 
 def w12_validate(mat: W12Matrix, ws: torch.Tensor, stream=None) -> int:
+    _check_ws(mat, ws)
     d = mat.desc()
     return int(lib().w12_validate(ctypes.byref(d), _ptr(ws), ws.numel(), _stream(stream)))
 
@@ -267,7 +320,7 @@ def encode(w: torch.Tensor, stream=None) -> W12Matrix:
     n_esc = w12_encode_plan(w, e_top, row_ptr, ws, stream)
     records = torch.empty((n // REC_ROWS) * (k // REC_COLS) * REC_BYTES, dtype=torch.uint8, device=dev)
     esc = torch.empty(max(n_esc, 1), dtype=torch.int64, device=dev)
-    w12_encode(w, e_top, row_ptr, records, esc if n_esc else None, stream)
+    w12_encode(w, e_top, row_ptr, records, esc if n_esc else None, stream, n_esc=n_esc)
     return W12Matrix(n, k, records, e_top, row_ptr, esc[:n_esc], n_esc)
 
 

@@ -92,10 +92,14 @@ def test_encode_argument_errors():
     assert lib.w12_encode_plan(FAKE, 1024, 1024, FAKE, FAKE, None, FAKE, 1 << 20, None) == w12.E_INVALID_ARG
     assert lib.w12_encode_plan(FAKE, 1024, 1024, FAKE, FAKE, ctypes.byref(n_esc), FAKE, 16, None) == \
         w12.E_WORKSPACE
-    assert lib.w12_encode(FAKE, 16, 512, FAKE, FAKE, 0, FAKE, None) == w12.E_INVALID_ARG
-    assert lib.w12_encode(FAKE + 4, 16, 512, FAKE, FAKE, FAKE, FAKE, None) == w12.E_INVALID_ARG
+    assert lib.w12_encode(FAKE, 16, 512, FAKE, FAKE, 0, FAKE, 8, None) == w12.E_INVALID_ARG
+    assert lib.w12_encode(FAKE + 4, 16, 512, FAKE, FAKE, FAKE, FAKE, 8, None) == w12.E_INVALID_ARG
+    # escapes need a buffer: NULL esc with a nonzero capacity, or a bad capacity, is refused
+    assert lib.w12_encode(FAKE, 16, 512, FAKE, FAKE, FAKE, None, 3, None) == w12.E_INVALID_ARG
+    assert lib.w12_encode(FAKE, 16, 512, FAKE, FAKE, FAKE, FAKE, -1, None) == w12.E_INVALID_ARG
+    assert lib.w12_encode(FAKE, 16, 512, FAKE, FAKE, FAKE, FAKE, 16 * 512 + 1, None) == w12.E_INVALID_ARG
     # a matrix whose escape count could overflow 32-bit CSR offsets is refused
-    assert lib.w12_encode(FAKE, 1 << 17, 1 << 16, FAKE, FAKE, FAKE, FAKE, None) == w12.E_UNSUPPORTED_SHAPE
+    assert lib.w12_encode(FAKE, 1 << 17, 1 << 16, FAKE, FAKE, FAKE, FAKE, 8, None) == w12.E_UNSUPPORTED_SHAPE
 
 
 def test_workspace_sizes():
@@ -210,3 +214,28 @@ def test_tuning_hooks_are_per_thread():
     finally:
         w12.set_tuning(w12.TUNE_GRID, old)
     assert seen["plan"] == base
+
+
+def test_wrappers_check_tensors_before_calling():
+    """The Python wrappers refuse host tensors, wrong dtypes and wrong shapes
+    before anything reaches the library (nothing here touches a GPU)."""
+    import torch
+    mat = w12.W12Matrix(32, 512, torch.zeros(2 * w12.REC_BYTES, dtype=torch.uint8),
+                        torch.zeros(32, dtype=torch.uint8), torch.zeros(33, dtype=torch.int32),
+                        torch.zeros(1, dtype=torch.int64), 0)
+    x = torch.zeros((4, 512), dtype=torch.bfloat16)
+    y = torch.zeros((4, 32), dtype=torch.float32)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device"):
+        w12.w12_gemm(mat, x, y, ws)
+    with pytest.raises(ValueError, match="device"):
+        w12.w12_gemm_q8(mat, x, y, 0, ws)
+    with pytest.raises(ValueError, match="device"):
+        w12.w12_lmhead_argmax(mat, x, torch.zeros(4, dtype=torch.int32), None, ws)
+    with pytest.raises(TypeError):
+        w12.w12_gemm(mat, torch.zeros((4, 512), dtype=torch.float32), y, ws)
+    with pytest.raises(ValueError, match="device"):
+        w12.w12_decode(mat, torch.zeros((32, 512), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="int64"):
+        w12.w12_encode(torch.zeros((32, 512), dtype=torch.int16), None, None, None,
+                       torch.zeros(4, dtype=torch.int32))

@@ -119,3 +119,25 @@ def test_workload_encode_full_parity(wl, mi):
     frac = mat.n_esc / w.size
     log(f"  n_esc={mat.n_esc} fraction={frac:.3e} bits/weight={o.bits_per_weight(spec.n, spec.k, mat.n_esc):.4f}")
     assert mat.nbytes() == o.encoded_nbytes(spec.n, spec.k, mat.n_esc)
+
+
+def test_encode_never_writes_past_escape_capacity():
+    """A buffer smaller than the escape count gets the list's prefix and not
+    one byte more; records and the CSR row pointers are unaffected."""
+    w = synth.workload_matrix(4, 0, rows=slice(0, 256))[:64]
+    ref = o.encode(w)
+    assert ref.n_esc > 40
+    wd = dev16(w)
+    e_top = torch.empty(64, dtype=torch.uint8, device="cuda")
+    row_ptr = torch.empty(65, dtype=torch.int32, device="cuda")
+    ws = w12.new_workspace(w12.OP_ENCODE_PLAN, 64, w.shape[1])
+    assert w12.w12_encode_plan(wd, e_top, row_ptr, ws) == ref.n_esc
+    cap = ref.n_esc - 37
+    records = torch.empty(ref.records.size, dtype=torch.uint8, device="cuda")
+    esc = torch.full((ref.n_esc + 8,), -1, dtype=torch.int64, device="cuda")
+    w12.w12_encode(wd, e_top, row_ptr, records, esc, n_esc=cap)
+    got = esc.cpu().numpy()
+    assert np.array_equal(got[:cap].view(o.ESC_DTYPE), ref.esc[:cap])
+    assert np.all(got[cap:] == -1)
+    assert np.array_equal(records.cpu().numpy(), ref.records)
+    assert np.array_equal(row_ptr.cpu().numpy().view(np.uint32), ref.row_ptr)
