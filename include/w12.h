@@ -47,7 +47,8 @@
  * ---------------------------------------------------------------- CONVENTIONS
  * - Every tensor pointer is a DEVICE pointer owned by the caller. Host pointers
  *   are the w12_matrix descriptor itself and n_esc_host. The library never
- *   allocates, frees or retains memory.
+ *   allocates, frees or retains memory, apart from the static scratch that
+ *   w12_gemm_noalloc uses (W12_NOALLOC_SCRATCH_BYTES per device).
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
  *   are asynchronous on it, except w12_encode_plan and w12_validate, which
  *   synchronize it. Inputs must stay valid until the stream work completes.
@@ -83,6 +84,7 @@ extern "C" {
 #define W12_REC_VIEW_BYTES 8192
 #define W12_MAX_M 64
 #define W12_WS_COUNTER_BYTES 16640 /* counter words at the start of a GEMM workspace */
+#define W12_NOALLOC_SCRATCH_BYTES (16u << 20) /* static scratch of w12_gemm_noalloc, per device */
 
 /* status codes */
 #define W12_OK 0
@@ -167,6 +169,20 @@ int w12_decode(const w12_matrix* m, uint16_t* w_out, void* stream);
  * ws: w12_workspace_bytes(W12_OP_GEMM, n, k, M) bytes (device). */
 int w12_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,
              int y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* w12_gemm without a workspace argument, for callers that cannot allocate
+ * device memory (code under graph capture, serving loops and harnesses that
+ * forbid hipMalloc). Same arguments, kernels and results as w12_gemm; the
+ * workspace is a static device array of W12_NOALLOC_SCRATCH_BYTES that each
+ * device holds until the process ends. A device's first call looks up its
+ * address and clears its counter words (a small kernel on `stream`); no call
+ * allocates or frees anything. W12_E_WORKSPACE when
+ * w12_workspace_bytes(W12_OP_GEMM, n, k, M) exceeds the scratch (nothing is
+ * launched). All calls on one device share its scratch: calls that may
+ * overlap on one device (different streams, or graphs replayed concurrently)
+ * race and give wrong results; serialize them or use w12_gemm. */
+int w12_gemm_noalloc(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,
+                     int y_dtype, void* stream);
 
 /* Q pass (section 4.3, zero-copy Q pass): the same product over the 8-bit
  * view only - the first 8 KB of each record - with the four dropped mantissa

@@ -3,11 +3,19 @@
 // call, so invalid arguments never launch anything.
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "w12_internal.h"
 
 using namespace w12;
+
+// The workspace of w12_gemm_noalloc: counter words and partial sums in a
+// file-scope device array instead of caller memory. Every device the library
+// runs on holds its own copy until the process ends. In host code the array's
+// name is no device address: host code uses only the address
+// hipGetSymbolAddress returns for the current device, kept per device.
+static __device__ __align__(256) uint8_t scratch[W12_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -193,6 +201,44 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   return W12_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_at[kMaxDevices];
+
+// Clears the counter words with plain vector stores (a kernel, not a memset
+// node, so the clear is safe inside a captured graph too).
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The scratch address on the current device. On a device's first call it is
+// looked up and its counter words cleared on `st`, ahead of the GEMM there.
+int scratch_on_device(void** out, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "gemm_noalloc: current device");
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = "gemm_noalloc: device ordinal " + std::to_string(dev) + " beyond the scratch table";
+    return W12_E_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_at[dev]) {
+    void* at = nullptr;
+    e = hipGetSymbolAddress(&at, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "gemm_noalloc: scratch address");
+    constexpr int kWords = (int)(kCounterBytes / sizeof(uint32_t));
+    hipLaunchKernelGGL(k_zero_words, dim3((kWords + 255) / 256), dim3(256), 0, st, reinterpret_cast<uint32_t*>(at),
+                       kWords);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "gemm_noalloc: counter clear");
+    g_scratch_at[dev] = at;
+  }
+  *out = g_scratch_at[dev];
+  return W12_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,6 +370,24 @@ int w12_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   const int s = check_gemm_args(m, x, M, ldx, y, ldy, y_dtype);
   if (s != W12_OK) return s;
   return run_gemm(m, x, M, ldx, y, ldy, y_dtype, W12_OP_GEMM, true, ws, ws_bytes, nullptr, nullptr, stream);
+}
+
+int w12_gemm_noalloc(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,
+                     int y_dtype, void* stream) {
+  const int s = check_gemm_args(m, x, M, ldx, y, ldy, y_dtype);
+  if (s != W12_OK) return s;
+  const size_t need = ws_bytes_any(m->n, m->k, M, W12_OP_GEMM);
+  if (need > W12_NOALLOC_SCRATCH_BYTES) {
+    g_last_error = "gemm_noalloc: this shape needs " + std::to_string(need) + " bytes of workspace, the static " +
+                   "scratch holds " + std::to_string((size_t)W12_NOALLOC_SCRATCH_BYTES) + "; use w12_gemm";
+    return W12_E_WORKSPACE;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const int r = scratch_on_device(&ws, st);
+  if (r != W12_OK) return r;
+  return run_gemm(m, x, M, ldx, y, ldy, y_dtype, W12_OP_GEMM, true, ws, W12_NOALLOC_SCRATCH_BYTES, nullptr, nullptr,
+                  stream);
 }
 
 int w12_gemm_q8(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy,

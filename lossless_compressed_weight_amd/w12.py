@@ -25,6 +25,7 @@ ABI_VERSION = 2
 FORMAT_VERSION = 1
 REC_ROWS, REC_COLS, REC_BYTES, REC_VIEW_BYTES = 16, 512, 12288, 8192
 MAX_M = 64
+NOALLOC_SCRATCH_BYTES = 16 << 20
 WS_COUNTER_BYTES = 16640
 OK, E_INVALID_ARG, E_UNSUPPORTED_SHAPE, E_M_RANGE, E_WORKSPACE, E_VERSION, E_HIP, E_NOT_IMPLEMENTED, E_CORRUPT = (
     0, -1, -2, -3, -4, -5, -6, -7, -8)
@@ -74,6 +75,7 @@ _SIGNATURES = {
     "w12_encode": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _I64, _P]),
     "w12_decode": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _P]),
     "w12_gemm": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _SZ, _P]),
+    "w12_gemm_noalloc": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _I64, ctypes.c_int, _P]),
     "w12_gemm_q8": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _I64, ctypes.c_int,
                                    ctypes.c_uint32, _P, _SZ, _P]),
     "w12_lmhead_argmax": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _P, _P, _SZ, _P]),
@@ -258,6 +260,15 @@ def w12_gemm(mat: W12Matrix, x, y, ws, stream=None):
     d = mat.desc()
     _check(lib().w12_gemm(ctypes.byref(d), _ptr(x), x.shape[0], x.stride(0), _ptr(y), y.stride(0), ydt,
                           _ptr(ws), ws.numel(), _stream(stream)), "w12_gemm")
+
+
+def w12_gemm_noalloc(mat: W12Matrix, x, y, stream=None):
+    """w12_gemm on the library's static per-device scratch (no workspace)."""
+    _check_x(mat, x)
+    ydt = _check_y(mat, y, x.shape[0])
+    d = mat.desc()
+    _check(lib().w12_gemm_noalloc(ctypes.byref(d), _ptr(x), x.shape[0], x.stride(0), _ptr(y), y.stride(0), ydt,
+                                  _stream(stream)), "w12_gemm_noalloc")
 
 
 def w12_gemm_q8(mat: W12Matrix, x, y, flags, ws, stream=None):

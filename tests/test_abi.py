@@ -239,3 +239,19 @@ def test_wrappers_check_tensors_before_calling():
     with pytest.raises(ValueError, match="int64"):
         w12.w12_encode(torch.zeros((32, 512), dtype=torch.int16), None, None, None,
                        torch.zeros(4, dtype=torch.int32))
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch():
+    """w12_gemm_noalloc checks its arguments and the workspace the shape needs
+    against the static scratch before any HIP call (fake pointers: nothing
+    may be launched)."""
+    lib = w12.lib()
+    big_k = 1 << 20
+    assert w12.workspace_bytes(w12.OP_GEMM, 16, big_k, 64) > w12.NOALLOC_SCRATCH_BYTES
+    m = w12.MatrixC(16, big_k, FAKE, FAKE, FAKE, 0, 0, w12.FORMAT_VERSION)
+    assert lib.w12_gemm_noalloc(ctypes.byref(m), FAKE, 64, big_k, FAKE, 16, w12.F32, None) == w12.E_WORKSPACE
+    assert b"scratch" in lib.w12_last_error()
+    m = w12.MatrixC(1024, 1024, FAKE, FAKE, FAKE, 0, 0, w12.FORMAT_VERSION)
+    assert lib.w12_gemm_noalloc(ctypes.byref(m), FAKE, 0, 1024, FAKE, 1024, w12.F32, None) == w12.E_M_RANGE
+    assert lib.w12_gemm_noalloc(ctypes.byref(m), FAKE, 4, 1000, FAKE, 1024, w12.F32, None) == w12.E_INVALID_ARG
+    assert lib.w12_gemm_noalloc(None, FAKE, 4, 1024, FAKE, 1024, w12.F32, None) == w12.E_INVALID_ARG
