@@ -293,11 +293,10 @@ def workloads(torch, w12, synth, dev, stream, reps):
     del mats
     # config 2: one decoder layer's seven GEMMs back to back at M = 32 and 64
     wl = synth.WORKLOADS[2]
-    layer = []
+    layer, wts = [], {}
     for i, spec in enumerate(wl.matrices):
-        wi = synth.workload_matrix(2, i)
-        layer.append(copies_of(w12, w12.encode(torch.from_numpy(wi.view(np.int16)).to(dev)), 3))
-        del wi
+        wts[spec.name] = torch.from_numpy(synth.workload_matrix(2, i).view(np.int16)).to(dev)
+        layer.append(copies_of(w12, w12.encode(wts[spec.name]), 3))
     packed = sum(c[0].n * c[0].k * 3 // 2 for c in layer)
     for m in (32, 64):
         xs = {k: torch.from_numpy(synth.make_activations(m, k, seed=synth.activation_seed(2, 0, m)).view(np.int16)).to(dev)
@@ -316,6 +315,8 @@ def workloads(torch, w12, synth, dev, stream, reps):
         out[f"config2_layer_m{m}"] = {"layer_us": round(lay, 1), "packed_gbs": round(packed / lay / 1e3, 1),
                                       "pct_peak": round(100 * packed / lay / 1e3 / PEAK_GBS, 2), "per_gemm": per}
     del layer
+    out.update(fused_layer(torch, w12, synth, dev, stream, reps, wts, packed))
+    del wts
     # config 3: LM head fused with the argmax at M = 1, 16, 32
     w = synth.workload_matrix(3, 0)
     mat = w12.encode(torch.from_numpy(w.view(np.int16)).to(dev))
@@ -333,24 +334,88 @@ def workloads(torch, w12, synth, dev, stream, reps):
             "pct_peak": round(100 * packed / us / 1e3 / PEAK_GBS, 2),
             "kernel": w12.plan_info(mat, w12.OP_LMHEAD_ARGMAX, m)["kernel_name"]}
     del mats, mat
-    # config 4: escape stress, exact GEMM and Q pass (view only) at M = 32
-    for i, spec in enumerate(synth.WORKLOADS[4].matrices):
-        wi = synth.workload_matrix(4, i)
+    # config 4: escape stress, exact GEMM and the two Q sources at M = 32; the
+    # same Q sources on the normal gate matrix of config 1 for comparison
+    for wl_i, i, tag in [(4, j, f"config4_{spec.name}_m32") for j, spec in enumerate(synth.WORKLOADS[4].matrices)] + \
+            [(1, 0, "config1_gate_q_sources_m32")]:
+        spec = synth.WORKLOADS[wl_i].matrices[i]
+        wi = synth.workload_matrix(wl_i, i)
         mat = w12.encode(torch.from_numpy(wi.view(np.int16)).to(dev))
         del wi
         mats = copies_of(w12, mat, 4)
-        x = torch.from_numpy(synth.make_activations(32, spec.k, seed=synth.activation_seed(4, i, 32)).view(np.int16)).to(dev)
+        x = torch.from_numpy(synth.make_activations(32, spec.k, seed=synth.activation_seed(wl_i, i, 32))
+                             .view(np.int16)).to(dev)
         y = torch.empty((32, spec.n), dtype=torch.bfloat16, device=dev)
         ws = w12.new_workspace(w12.OP_GEMM, spec.n, spec.k, 32, dev)
         ue = time_shape(torch, w12, stream, mats, x, y, ws, max(4, reps // 2))
         uq = time_shape(torch, w12, stream, mats, x, y, ws, reps, op="q8")
-        view = spec.n * spec.k
-        out[f"config4_{spec.name}_m32"] = {
-            "exact_us": round(ue, 2), "exact_kernel": w12.plan_info(mat, w12.OP_GEMM, 32)["kernel_name"],
-            "n_esc": mat.n_esc, "q_view_us": round(uq, 2), "q_view_gbs": round(view / uq / 1e3, 1),
-            "q_kernel": w12.plan_info(mat, w12.OP_GEMM_Q8, 32)["kernel_name"]}
+        uqe = time_shape(torch, w12, stream, mats, x, y, ws, max(4, reps // 2), op="q8", q_flags=w12.Q8_APPLY_ESCAPES)
+        out[tag] = {"n": spec.n, "k": spec.k, "n_esc": mat.n_esc,
+                    "exact_us": round(ue, 2), "exact_kernel": w12.plan_info(mat, w12.OP_GEMM, 32)["kernel_name"],
+                    "q_view_us": round(uq, 2), "q_view_gbs": round(spec.n * spec.k / uq / 1e3, 1),
+                    "q_view_escapes_us": round(uqe, 2),
+                    "q_kernel": w12.plan_info(mat, w12.OP_GEMM_Q8, 32)["kernel_name"]}
+        out[tag].update(q_source_agreement(torch, w12, mat, x))
         del mats, mat
     return out
+
+
+def fused_layer(torch, w12, synth, dev, stream, reps, wts, packed):
+    """The same layer with q|k|v and gate|up encoded as row concatenations
+    (four GEMMs instead of seven), issued eagerly and replayed as one HIP graph
+    per weight copy."""
+    groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    fused = [copies_of(w12, w12.encode(torch.cat([wts[p] for p in g])), 3) for g in groups]
+    out = {}
+    for m in (32, 64):
+        xs = {k: torch.from_numpy(synth.make_activations(m, k, seed=synth.activation_seed(2, 0, m)).view(np.int16)).to(dev)
+              for k in (5120, 6144, 17408)}
+        ys = [torch.empty((m, c[0].n), dtype=torch.bfloat16, device=dev) for c in fused]
+        wss = [w12.new_workspace(w12.OP_GEMM, c[0].n, c[0].k, m, dev) for c in fused]
+        per = {}
+        for gi, (g, c) in enumerate(zip(groups, fused)):
+            us = time_shape(torch, w12, stream, c, xs[c[0].k], ys[gi], wss[gi], reps)
+            per["|".join(g)] = {"us": round(us, 2), "kernel": w12.plan_info(c[0], w12.OP_GEMM, m)["kernel_name"]}
+
+        def layer(r, st=stream):
+            for gi, c in enumerate(fused):
+                w12.w12_gemm(c[r % len(c)], xs[c[0].k], ys[gi], wss[gi], st)
+        eager = back_to_back_us(torch, stream, layer, reps)
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            layer(0, side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        for r in range(3):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layer(r, torch.cuda.current_stream())
+            graphs.append(g)
+        torch.cuda.synchronize()
+        graph_us = back_to_back_us(torch, stream, lambda r: graphs[r % 3].replay(), reps)
+        out[f"config2_fused_layer_m{m}"] = {
+            "gemms": 4, "layer_us": round(eager, 1), "packed_gbs": round(packed / eager / 1e3, 1),
+            "graph_layer_us": round(graph_us, 1), "graph_packed_gbs": round(packed / graph_us / 1e3, 1),
+            "graph_pct_peak": round(100 * packed / graph_us / 1e3 / PEAK_GBS, 2), "per_gemm": per}
+        del graphs
+    return out
+
+
+def q_source_agreement(torch, w12, mat, x):
+    """Per activation row, does the argmax over the N outputs of a Q source
+    equal that of the exact GEMM? For the 8-bit view alone and the view with
+    the escapes applied, beside the bytes each source reads per call."""
+    m, n, k = x.shape[0], mat.n, mat.k
+    ye = w12.gemm(mat, x, torch.float32).argmax(dim=1)
+    yq = w12.gemm_q8(mat, x, torch.float32).argmax(dim=1)
+    yqe = w12.gemm_q8(mat, x, torch.float32, apply_escapes=True).argmax(dim=1)
+    act = 2 * m * k + 2 * m * n
+    return {"agree_q_view": round(float((yq == ye).float().mean()), 4),
+            "agree_q_view_escapes": round(float((yqe == ye).float().mean()), 4),
+            "bytes_exact": algo_bytes(mat, m), "bytes_q_view": n * k + n + act,
+            "bytes_q_view_escapes": n * k + n + 4 * (n + 1) + 8 * mat.n_esc + act}
 
 
 # ------------------------------------------------------------------ main

@@ -79,6 +79,15 @@ def check_bf16(y_bf16_bits: np.ndarray, y_f32: np.ndarray, y64: np.ndarray, what
     assert float(err.max()) <= REL + BF16_ULP, f"{what}: BF16 error {float(err.max()):.3e}"
 
 
+def check_bf16_value(y_bf16_bits: np.ndarray, y64: np.ndarray, what: str):
+    """A BF16 output on its own (no fp32 twin): within (2e-3 + 2^-8) of y64."""
+    yb = o.bf16_to_f64(y_bf16_bits)
+    s = np.max(np.abs(y64), axis=1, keepdims=True)
+    denom = np.maximum(np.abs(y64), FLOOR * s)
+    err = np.abs(yb - y64) / np.where(denom > 0, denom, 1.0)
+    assert float(err.max()) <= REL + BF16_ULP, f"{what}: BF16 error {float(err.max()):.3e}"
+
+
 def argmax_logits_f32(mat, x_dev):
     """fp32 logits from the kernel the fused argmax runs (the helper-wave MFMA
     kernel from 3 activation rows, the GEMV below), so that the argmax can be
