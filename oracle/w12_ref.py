@@ -296,3 +296,56 @@ def argmax_ref(y: np.ndarray):
     else:
         margin = np.full(y.shape[0], np.inf)
     return idx.astype(np.int64), margin
+
+
+# --- certified LM head ------------------------------------------------------------
+# SpecPilot section 4.1, the certified LM head paragraph: a Q copy of the head
+# plus a per-row Cauchy-Schwarz bound on its error proves which vocabulary rows
+# cannot be the argmax; only the rest are rescored with the exact weights, and
+# the full head runs when too many remain. [reading F16] the Q copy is the
+# zero-copy 8-bit view with the escapes applied (section 4.3), so the bound
+# covers the four dropped mantissa bits of in-window weights only.
+def q_view_escapes_bits(enc: Encoded) -> np.ndarray:
+    """The 8-bit view with every escape replaced by its exact bits."""
+    q = q_view_bits(enc)
+    q[_escape_rows(enc), enc.esc["col"].astype(np.int64)] = enc.esc["bits"]
+    return q
+
+
+def certify_bounds(enc: Encoded):
+    """Per row n: r_n = ||w_n - q_n||_2 (q: the view with escapes applied),
+    and a_n = ||w_n||_2 + ||v_n||_2 (v: the view with the placeholders), the
+    scale of the fp32 rounding allowance. A row holding inf or NaN gets
+    r_n = a_n = +inf (it can never be ruled out)."""
+    w = bf16_to_f64(decode(enc))
+    v = bf16_to_f64(q_view_bits(enc))
+    q = bf16_to_f64(q_view_escapes_bits(enc))
+    bad = ~np.isfinite(w).all(axis=1)
+    w = np.where(np.isfinite(w), w, 0.0)
+    q = np.where(np.isfinite(q), q, 0.0)
+    r = np.sqrt(np.sum((w - q) ** 2, axis=1))
+    a = np.sqrt(np.sum(w ** 2, axis=1)) + np.sqrt(np.sum(v ** 2, axis=1))
+    r[bad] = np.inf
+    a[bad] = np.inf
+    return r, a
+
+
+def certify_slack(k: int) -> float:
+    """[reading F16] the fp32 rounding allowance per unit of ||x|| a_n: four
+    times gamma_K = K u / (1 - K u), u = 2^-24, which bounds the rounding
+    error of any fp32 summation order of K products (and of the escape
+    fix-up's terms, whose magnitudes a_n also covers) with room for a
+    non-round-to-nearest accumulator."""
+    u = 2.0 ** -24
+    return 4.0 * k * u / (1.0 - k * u)
+
+
+def certified_survivors(lq: np.ndarray, r: np.ndarray, a: np.ndarray, x_norm: float, slack: float) -> np.ndarray:
+    """Rows whose logit may be the largest: row n is ruled out when its upper
+    bound lq_n + ||x|| (r_n + slack a_n) is below the largest lower bound
+    lq_j - ||x|| (r_j + slack a_j). lq: Q-copy logits of one activation row."""
+    width = x_norm * (r + slack * a)
+    lower = np.where(np.isfinite(width), lq - width, -np.inf)
+    best_lower = np.max(lower[~np.isnan(lower)]) if np.any(~np.isnan(lower)) else -np.inf
+    upper = lq + width
+    return np.flatnonzero(~(upper < best_lower))

@@ -390,3 +390,81 @@ def test_argmax_planted_winners():
     tie[0, [2, 5]] = 1.0
     idx, margin = o.argmax_ref(tie)
     assert idx[0] == 2 and margin[0] == 0.0
+
+
+# --- certified LM head (section 4.1, certified LM head paragraph) --------------
+def test_certify_bounds_zero_when_low_bits_are_midpoint():
+    """Every in-window weight already at the midpoint nibble and escapes
+    restored exactly: the Q copy equals the weights, so r = 0, and a is twice
+    the row norm (view and weights agree)."""
+    w = synth.plain_gaussian(32, 1024, seed=12)
+    w = (w & 0xFFF0) | 0x0008
+    w[3, 7] = 0                       # an escape (zero) in a row
+    w[5, 9] = w[5, 9] + (30 << 7)     # an escape far above the window
+    enc = o.encode(w)
+    assert enc.n_esc >= 2
+    r, a = o.certify_bounds(enc)
+    assert np.all(r == 0.0)
+    wf = o.bf16_to_f64(w)
+    clean = [i for i in range(32) if i not in (3, 5)]
+    assert np.allclose(a[clean], 2 * np.sqrt((wf[clean] ** 2).sum(1)), rtol=1e-15)
+
+
+def test_certify_bounds_closed_form_single_weight():
+    """One weight off the midpoint by d nibble steps at exponent e: the Q copy
+    differs only there, by d * 2^(e - 7), so r is that amount exactly."""
+    base = np.full((16, 512), 0x3F88, np.uint16)     # 1.0625: exponent 127, nibble 8
+    for d, (row, col) in zip((-8, -1, 1, 7), ((0, 0), (1, 100), (2, 511), (3, 250))):
+        base[row, col] = 0x3F80 | (8 + d)            # nibble 8 + d
+    base[4, 3] = 0x4088 | 0x3                        # exponent 129, nibble 11: d = 3
+    enc = o.encode(base)
+    assert enc.n_esc == 0
+    r, _ = o.certify_bounds(enc)
+    want = np.zeros(16)
+    want[:4] = np.abs([-8, -1, 1, 7]) * 2.0 ** -7
+    want[4] = 3 * 2.0 ** (2 - 7)
+    assert np.array_equal(r, want)
+
+
+def test_certify_bounds_cauchy_schwarz_and_non_finite():
+    """|x.w - x.q| <= ||x|| r on random rows, with equality when x points along
+    w - q; a row with inf or NaN gets infinite bounds."""
+    w = synth.workload_matrix(0, 0)[:64].copy()
+    w[10, 5] = 0x7F80
+    w[11, 6] = 0x7FC1
+    enc = o.encode(w)
+    r, a = o.certify_bounds(enc)
+    assert np.isinf(r[10]) and np.isinf(r[11]) and np.isinf(a[10]) and np.isinf(a[11])
+    fin = np.isfinite(r)
+    wf = o.bf16_to_f64(w)[fin]
+    q = o.bf16_to_f64(o.q_view_escapes_bits(enc))[fin]
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        x = rng.normal(size=1024)
+        assert np.all(np.abs((wf - q) @ x) <= np.linalg.norm(x) * r[fin] * (1 + 1e-12))
+    d = wf[0] - q[0]
+    assert math.isclose(abs(d @ d), np.linalg.norm(d) * r[fin][0], rel_tol=1e-12)
+
+
+def test_certified_survivors_keep_the_argmax():
+    """The rows kept always include the true argmax; with a zero bound and no
+    rounding allowance only the argmax survives (distinct logits)."""
+    rng = np.random.default_rng(11)
+    for trial in range(50):
+        n = 300
+        l = rng.normal(size=n) * 3
+        r = np.abs(rng.normal(size=n)) * 0.02
+        x_norm = 10.0
+        err = rng.uniform(-1, 1, size=n) * x_norm * r          # any error within the bound
+        lq = l - err
+        keep = o.certified_survivors(lq, r, np.ones(n), x_norm, 0.0)
+        assert int(np.argmax(l)) in keep
+        assert len(o.certified_survivors(l, np.zeros(n), np.ones(n), x_norm, 0.0)) == 1
+    # an infinite bound (non-finite row) is never ruled out and rules nothing out
+    lq = np.array([1.0, 5.0, 2.0])
+    keep = o.certified_survivors(lq, np.array([0.0, 0.0, np.inf]), np.ones(3), 1.0, 0.0)
+    assert list(keep) == [1, 2]
+    # a NaN logit (a row holding NaN) gives a NaN upper bound: kept, not dropped
+    keep = o.certified_survivors(np.array([1.0, 5.0, np.nan]), np.array([0.0, 0.0, np.inf]), np.ones(3), 1.0, 0.0)
+    assert list(keep) == [1, 2]
+    assert o.certify_slack(5120) == pytest.approx(4 * 5120 * 2.0 ** -24, rel=1e-3)

@@ -85,6 +85,17 @@ MUTANTS = [
         "u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)", 1)]),
     ("size_drops_row_ptr_sentinel", [(
         "4 * (n + 1)", "4 * n", 1)]),
+    ("certify_q_copy_keeps_placeholders", [(
+        "q = bf16_to_f64(q_view_escapes_bits(enc))", "q = bf16_to_f64(q_view_bits(enc))", 1)]),
+    ("certify_bound_squared_norm", [(
+        "r = np.sqrt(np.sum((w - q) ** 2, axis=1))", "r = np.sum((w - q) ** 2, axis=1)", 1)]),
+    ("certify_non_finite_rows_bounded", [(
+        "    r[bad] = np.inf\n", "", 1)]),
+    ("survivors_lower_bound_sign", [(
+        "lower = np.where(np.isfinite(width), lq - width, -np.inf)",
+        "lower = np.where(np.isfinite(width), lq + width, -np.inf)", 1)]),
+    ("survivors_nan_upper_dropped", [(
+        "return np.flatnonzero(~(upper < best_lower))", "return np.flatnonzero(upper >= best_lower)", 1)]),
 ]
 
 # cheap pins first; a mutant stops at the first pin it breaks
