@@ -322,6 +322,7 @@ def workloads(torch, w12, synth, dev, stream, reps):
     mat = w12.encode(torch.from_numpy(w.view(np.int16)).to(dev))
     del w
     mats = copies_of(w12, mat, 2)
+    bounds = [w12.certify_bounds(c) for c in mats]
     packed = mat.n * mat.k * 3 // 2
     for m in (1, 16, 32):
         x = torch.from_numpy(synth.make_activations(m, 5120, seed=synth.activation_seed(3, 0, m)).view(np.int16)).to(dev)
@@ -333,7 +334,18 @@ def workloads(torch, w12, synth, dev, stream, reps):
             "us": round(us, 2), "packed_gbs": round(packed / us / 1e3, 1),
             "pct_peak": round(100 * packed / us / 1e3 / PEAK_GBS, 2),
             "kernel": w12.plan_info(mat, w12.OP_LMHEAD_ARGMAX, m)["kernel_name"]}
-    del mats, mat
+        # the certified head on the same inputs: Q pass + bounds + rescoring
+        sv = torch.empty(m, dtype=torch.int32, device=dev)
+        wsc = w12.new_workspace(w12.OP_LMHEAD_CERTIFIED, mat.n, mat.k, m, dev)
+        uc = back_to_back_us(torch, stream, lambda i: w12.w12_lmhead_argmax_certified(
+            mats[i % len(mats)], bounds[i % len(mats)], x, idx, mx, sv, wsc, stream), max(4, reps // 3))
+        cidx = idx.clone()
+        w12.w12_lmhead_argmax(mat, x, idx, mx, ws, stream)
+        out[f"config3_lmhead_certified_m{m}"] = {
+            "us": round(uc, 2), "speedup_vs_fused_head": round(us / uc, 3),
+            "survivors_max": int(sv.max()), "fallback": bool(int(sv.max()) > w12.CERT_MAX_SURVIVORS),
+            "same_indices_as_fused_head": bool(torch.equal(cidx, idx))}
+    del mats, mat, bounds
     # config 4: escape stress, exact GEMM and the two Q sources at M = 32; the
     # same Q sources on the normal gate matrix of config 1 for comparison
     for wl_i, i, tag in [(4, j, f"config4_{spec.name}_m32") for j, spec in enumerate(synth.WORKLOADS[4].matrices)] + \

@@ -106,6 +106,9 @@ extern "C" {
 #define W12_OP_GEMM 2
 #define W12_OP_GEMM_Q8 3
 #define W12_OP_LMHEAD_ARGMAX 4
+#define W12_OP_LMHEAD_CERTIFIED 5
+
+#define W12_CERT_MAX_SURVIVORS 256 /* rows rescored per activation row before the full head runs */
 
 /* w12_gemm_q8 flags */
 #define W12_Q8_APPLY_ESCAPES 1u
@@ -199,6 +202,34 @@ int w12_gemm_q8(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, 
  * ws: w12_workspace_bytes(W12_OP_LMHEAD_ARGMAX, n, k, M). */
 int w12_lmhead_argmax(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, int32_t* idx,
                       float* max_logit, void* ws, size_t ws_bytes, void* stream);
+
+/* Certified argmax LM head (section 4.1, the certified LM head paragraph;
+ * section 4.3, zero-copy Q pass), step 1, once per matrix: per-row bounds
+ * for the Q copy, which is the 8-bit view with the escapes applied.
+ * bounds: device float[2 N] (8-byte aligned): bounds[2n] = r_n =
+ * ||w_n - q_n||_2 and bounds[2n+1] = a_n = ||w_n||_2 + ||v_n||_2 (w exact
+ * weights, q the Q copy, v the view with its placeholders), both summed in
+ * float64 and rounded up; +inf for a row holding inf or NaN. */
+int w12_certify_bounds(const w12_matrix* m, float* bounds, void* stream);
+
+/* Certified argmax LM head, per call: the same idx (and max_logit) contract as
+ * w12_lmhead_argmax. A Q pass (w12_gemm_q8 with W12_Q8_APPLY_ESCAPES) gives
+ * fp32 logits lq; with c = 4 K u / (1 - K u), u = 2^-24, row n is ruled out
+ * when lq_n + ||x|| (r_n + c a_n) < max_j (lq_j - ||x|| (r_j + c a_j)), which
+ * no row holding the largest exact logit can meet. The rows left are rescored
+ * exactly (fp32 sums of the exact weights, placeholders swapped for the
+ * escapes' values); the lowest index wins equal values. When any activation
+ * row keeps more than W12_CERT_MAX_SURVIVORS rows, the full fused head
+ * (w12_lmhead_argmax) runs for the call instead; it is always enqueued and
+ * does nothing otherwise, so the call never synchronizes. max_logit is the
+ * rescored fp32 logit (its summation order differs from the full head's).
+ * survivors (nullable): M int32 counts of rows kept per activation row (above
+ * the cap: the full head ran). bounds: from w12_certify_bounds.
+ * ws: w12_workspace_bytes(W12_OP_LMHEAD_CERTIFIED, n, k, M), zero before its
+ * first use; every call leaves it ready for the next. */
+int w12_lmhead_argmax_certified(const w12_matrix* m, const float* bounds, const uint16_t* x, int64_t M,
+                                int64_t ldx, int32_t* idx, float* max_logit, int32_t* survivors, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* Checks a descriptor's device arrays: e_top in [16, 254], esc_row_ptr
  * starting at 0, nondecreasing and ending at n_esc, escape columns < K and

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libw12.so")
-SOURCES = ["w12_gemm.hip", "w12_gemm_mx.hip", "w12_api.hip", "w12_encode.hip", "w12_probe.hip"]
+SOURCES = ["w12_gemm.hip", "w12_gemm_mx.hip", "w12_api.hip", "w12_encode.hip", "w12_certify.hip", "w12_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

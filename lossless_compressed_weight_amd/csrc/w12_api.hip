@@ -3,6 +3,7 @@
 // call, so invalid arguments never launch anything.
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -104,6 +105,25 @@ int choose_kernel(int64_t n, int64_t k, int64_t n_esc, int64_t M, int op, bool f
   return W12_KERNEL_MFMA_HELPER;
 }
 
+size_t ws_bytes_any(int64_t n, int64_t k, int64_t M, int op);
+
+// Workspace of the certified head: [GEMM region shared by the Q pass and the
+// gated full head | CertState | Q logits [M][N] | chunk upper bounds | lists].
+struct CertLayout {
+  size_t gemm, state, logits, ub, list, total;
+};
+CertLayout cert_layout(int64_t n, int64_t k, int64_t M) {
+  CertLayout c{};
+  const size_t g = std::max(ws_bytes_any(n, k, M, W12_OP_GEMM_Q8), ws_bytes_any(n, k, M, W12_OP_LMHEAD_ARGMAX));
+  c.gemm = round256(g);
+  c.state = c.gemm;
+  c.logits = c.state + round256(sizeof(CertState));
+  c.ub = c.logits + round256((size_t)M * (size_t)n * sizeof(float));
+  c.list = c.ub + round256((size_t)M * (size_t)cert_chunks(n) * sizeof(float));
+  c.total = c.list + round256((size_t)M * W12_CERT_MAX_SURVIVORS * sizeof(uint32_t));
+  return c;
+}
+
 // Every plan a GEMM op may run for this shape fits in this much workspace.
 size_t ws_bytes_any(int64_t n, int64_t k, int64_t M, int op) {
   size_t b = gemm_ws_bytes(make_plan(n, k, M, op));
@@ -143,10 +163,14 @@ int run_mx(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void*
   return W12_OK;
 }
 
+// gate: null, or a device word that a kernel on the stream writes before this
+// call's kernels run; they do nothing when it is zero (helper-wave kernels only).
 int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
-             int op, bool fix, void* ws, size_t ws_bytes, int32_t* idx, float* maxv, void* stream) {
+             int op, bool fix, void* ws, size_t ws_bytes, int32_t* idx, float* maxv, void* stream,
+             const uint32_t* gate = nullptr) {
   const GemmPlan pl = make_plan(m->n, m->k, M, op);
-  const int kernel = choose_kernel(m->n, m->k, m->n_esc, M, op, fix, pl);
+  const int kernel = gate ? (pl.mfma ? W12_KERNEL_MFMA_HELPER : W12_KERNEL_GEMV)
+                          : choose_kernel(m->n, m->k, m->n_esc, M, op, fix, pl);
   if (kernel == W12_KERNEL_MFMA_STREAM) return run_mx(m, x, M, ldx, y, ldy, y_dtype, op, fix, ws, ws_bytes, stream);
   if (!pl.mfma && M > 16) return W12_E_M_RANGE;
   const size_t need = gemm_ws_bytes(pl);
@@ -175,6 +199,7 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   p.mode = op == W12_OP_LMHEAD_ARGMAX ? kModeArgmax : kModeStore;
   p.fix = fix && m->n_esc > 0;
   p.q = op == W12_OP_GEMM_Q8;
+  p.gate = gate;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // The helper-wave MFMA kernel's escape fix-up needs the activations of each
   // escape column for all rows. With many escapes per row it reads them from
@@ -189,7 +214,7 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
     char* xt_at = wsb + round256(pl.ctr_bytes) + round256(pl.part_bytes) + round256(pl.key_bytes);
     uint16_t* xt = (p.fix && m->n_esc * mm > kXtEscRowLines * m->n) ? reinterpret_cast<uint16_t*>(xt_at) : nullptr;
     uint16_t* xk = reinterpret_cast<uint16_t*>(xt_at + round256(pl.xt_bytes));
-    const hipError_t ex = launch_xpose(x, ldx, (int)M, (int)mm, (int)m->k, xt, xk, st);
+    const hipError_t ex = launch_xpose(x, ldx, (int)M, (int)mm, (int)m->k, xt, xk, gate, st);
     if (ex != hipSuccess) return hip_fail(ex, "activation transpose launch");
     p.xt = xt;
     p.xk = xk;
@@ -277,8 +302,10 @@ int64_t w12_set_tuning(int key, int64_t value) {
 size_t w12_workspace_bytes(int op, int64_t n, int64_t k, int64_t m) {
   if (check_shape(n, k) != W12_OK) return 0;
   if (op == W12_OP_ENCODE_PLAN) return round256((size_t)n * sizeof(uint32_t));
-  if (op != W12_OP_GEMM && op != W12_OP_GEMM_Q8 && op != W12_OP_LMHEAD_ARGMAX) return 0;
+  if (op != W12_OP_GEMM && op != W12_OP_GEMM_Q8 && op != W12_OP_LMHEAD_ARGMAX && op != W12_OP_LMHEAD_CERTIFIED)
+    return 0;
   if (m < 1 || m > W12_MAX_M) return 0;
+  if (op == W12_OP_LMHEAD_CERTIFIED) return cert_layout(n, k, m).total;
   return ws_bytes_any(n, k, m, op);
 }
 
@@ -405,6 +432,39 @@ int w12_lmhead_argmax(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t
   if (s != W12_OK) return s;
   return run_gemm(m, x, M, ldx, nullptr, 0, W12_F32, W12_OP_LMHEAD_ARGMAX, true, ws, ws_bytes, idx, max_logit,
                   stream);
+}
+
+int w12_certify_bounds(const w12_matrix* m, float* bounds, void* stream) {
+  const int s = check_matrix(m);
+  if (s != W12_OK) return s;
+  if (!bounds || (reinterpret_cast<uintptr_t>(bounds) & 7u) != 0) return W12_E_INVALID_ARG;
+  const hipError_t e = launch_cert_bounds(m, bounds, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "certify bounds kernel");
+  return W12_OK;
+}
+
+int w12_lmhead_argmax_certified(const w12_matrix* m, const float* bounds, const uint16_t* x, int64_t M,
+                                int64_t ldx, int32_t* idx, float* max_logit, int32_t* survivors, void* ws,
+                                size_t ws_bytes, void* stream) {
+  const int s = check_gemm_args(m, x, M, ldx, idx, m ? m->n : 0, W12_F32);
+  if (s != W12_OK) return s;
+  if (!bounds) return W12_E_INVALID_ARG;
+  const CertLayout c = cert_layout(m->n, m->k, M);
+  if (!ws || ws_bytes < c.total) return W12_E_WORKSPACE;
+  char* wsb = reinterpret_cast<char*>(ws);
+  CertState* st = reinterpret_cast<CertState*>(wsb + c.state);
+  float* lq = reinterpret_cast<float*>(wsb + c.logits);
+  // 1. Q-copy logits: the view with the escapes applied, fp32
+  int r = run_gemm(m, x, M, ldx, lq, m->n, W12_F32, W12_OP_GEMM_Q8, true, ws, c.gemm, nullptr, nullptr, stream);
+  if (r != W12_OK) return r;
+  // 2. bounds, survivors, exact rescoring, indices
+  const hipError_t e = launch_cert(m, x, ldx, (int)M, lq, bounds, st, reinterpret_cast<float*>(wsb + c.ub),
+                                   reinterpret_cast<uint32_t*>(wsb + c.list), idx, max_logit, survivors,
+                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "certified head kernels");
+  // 3. the full fused head, which does nothing unless the fallback flag is up
+  return run_gemm(m, x, M, ldx, nullptr, 0, W12_F32, W12_OP_LMHEAD_ARGMAX, true, ws, c.gemm, idx, max_logit, stream,
+                  &st->flag);
 }
 
 int w12_validate(const w12_matrix* m, void* ws, size_t ws_bytes, void* stream) {

@@ -1154,6 +1154,7 @@ struct GemvLds {
 template <int M, bool Q>
 __global__ __launch_bounds__(kThreads) void k_gemv(GemmParams a, const uint16_t* __restrict__ x) {
   __shared__ GemvLds<M> sh;
+  if (gated_off(a.gate)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x;
@@ -1316,6 +1317,7 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
 template <int MT, bool Q, int TB>
 __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
   __shared__ MfmaLds<MT> sh;
+  if (gated_off(a.gate)) return;
   constexpr int R = kMfmaR<MT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1379,8 +1381,10 @@ __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
 // columns per workgroup through LDS, read in 16-byte pieces along rows of x and
 // written in 16-byte pieces.
 __global__ __launch_bounds__(256) void k_xpose(const uint16_t* __restrict__ x, int64_t ldx, int M, int MM,
-                                               uint16_t* __restrict__ xt, uint16_t* __restrict__ xk) {
+                                               uint16_t* __restrict__ xt, uint16_t* __restrict__ xk,
+                                               const uint32_t* __restrict__ gate) {
   __shared__ uint16_t t[64][32 + 8];  // [m][column], rows padded to keep 16-byte alignment
+  if (gated_off(gate)) return;
   const int c0 = blockIdx.x * 32;
   // MM rows x 4 pieces of 8 columns
   for (int i = threadIdx.x; i < MM * 4; i += 256) {
@@ -1415,9 +1419,9 @@ __global__ __launch_bounds__(256) void k_xpose(const uint16_t* __restrict__ x, i
 }
 
 hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, uint16_t* xt, uint16_t* xk,
-                        hipStream_t s) {
+                        const uint32_t* gate, hipStream_t s) {
   if (mm > 64 || mm % 16 != 0 || M > mm || K % 64 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_xpose, dim3(K / 32), dim3(256), 0, s, x, ldx, M, mm, xt, xk);
+  hipLaunchKernelGGL(k_xpose, dim3(K / 32), dim3(256), 0, s, x, ldx, M, mm, xt, xk, gate);
   return hipGetLastError();
 }
 

@@ -175,9 +175,18 @@ struct GemmParams {
   int mode;                  // 0 = store Y, 1 = argmax keys
   int fix;                   // apply the escape fix-up
   int q;                     // Q pass (fix-up subtracts the Q view of the placeholder)
+  const uint32_t* gate;      // null, or a device word: the kernel does nothing when it reads 0
 };
 
 enum { kModeStore = 0, kModeArgmax = 1 };
+
+// A launch-time switch written by an earlier kernel on the same stream: every
+// workgroup reads it first and returns at once when it is zero (all of a
+// workgroup's threads read the same word, so they leave together, before any
+// barrier). Read with an agent-scope load so no stale cached copy is seen.
+__device__ __forceinline__ bool gated_off(const uint32_t* gate) {
+  return gate != nullptr && __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
+}
 
 // launchers (return a hipError_t)
 hipError_t launch_plan(const uint16_t* w, int n, int k, uint8_t* e_top, uint32_t* cnt, hipStream_t s);
@@ -206,6 +215,24 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t grid_override);
 hipError_t launch_gemm(const GemmPlan& plan, GemmParams p, hipStream_t s, int* unsupported);
+
+// ------------------------------------------------------------------ certified LM head
+// Per-call state of the certified head (w12_certify.hip), in the workspace;
+// zero before a workspace's first use and cleared again by every call (the
+// fallback flag and the norms are rewritten each call).
+constexpr int kCertMaxM = 64;
+struct CertState {
+  unsigned long long best[kCertMaxM];  // argmax keys of the rescored rows
+  double xnorm[kCertMaxM];             // ||x_m||_2
+  uint32_t lower[kCertMaxM];           // order-preserving key of the best lower bound
+  uint32_t count[kCertMaxM];           // surviving rows
+  uint32_t flag;                       // nonzero: some activation row kept more than the cap
+};
+int cert_chunks(int64_t n);
+hipError_t launch_cert_bounds(const w12_matrix* m, float* bounds, hipStream_t s);
+hipError_t launch_cert(const w12_matrix* mat, const uint16_t* x, int64_t ldx, int M, const float* lq,
+                       const float* bounds, CertState* st, float* ub_chunk, uint32_t* list, int32_t* idx,
+                       float* maxv, int32_t* survivors, hipStream_t s);
 
 // ------------------------------------------------------------------ stream kernel
 // The MFMA stream kernel (w12_gemm_mx.hip): eight streaming waves per
@@ -256,6 +283,7 @@ hipError_t launch_mx(const MxPlan& plan, MxParams p, hipStream_t s);
 // x [M, K] (row stride ldx) -> xt [K, mm] (mm = 16 * ceil(M / 16)) and xk (MFMA operand order), rows
 // past M zero; either output may be null.
 hipError_t launch_xpose(const uint16_t* x, int64_t ldx, int M, int mm, int K, uint16_t* xt, uint16_t* xk,
+                        const uint32_t* gate,
                         hipStream_t s);
 
 }  // namespace w12

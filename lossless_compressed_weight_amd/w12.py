@@ -30,7 +30,8 @@ WS_COUNTER_BYTES = 16640
 OK, E_INVALID_ARG, E_UNSUPPORTED_SHAPE, E_M_RANGE, E_WORKSPACE, E_VERSION, E_HIP, E_NOT_IMPLEMENTED, E_CORRUPT = (
     0, -1, -2, -3, -4, -5, -6, -7, -8)
 BF16, F32 = 0, 1
-OP_ENCODE_PLAN, OP_GEMM, OP_GEMM_Q8, OP_LMHEAD_ARGMAX = 1, 2, 3, 4
+OP_ENCODE_PLAN, OP_GEMM, OP_GEMM_Q8, OP_LMHEAD_ARGMAX, OP_LMHEAD_CERTIFIED = 1, 2, 3, 4, 5
+CERT_MAX_SURVIVORS = 256
 Q8_APPLY_ESCAPES = 1
 TUNE_PATH, TUNE_GRID = 1, 2
 KERNEL_GEMV, KERNEL_MFMA_HELPER, KERNEL_MFMA_STREAM = 1, 2, 3
@@ -75,6 +76,9 @@ _SIGNATURES = {
     "w12_encode": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _I64, _P]),
     "w12_decode": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _P]),
     "w12_gemm": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _SZ, _P]),
+    "w12_certify_bounds": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _P]),
+    "w12_lmhead_argmax_certified": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _P, _I64, _I64, _P, _P, _P, _P,
+                                                   _SZ, _P]),
     "w12_gemm_noalloc": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _I64, ctypes.c_int, _P]),
     "w12_gemm_q8": (ctypes.c_int, [ctypes.POINTER(MatrixC), _P, _I64, _I64, _P, _I64, ctypes.c_int,
                                    ctypes.c_uint32, _P, _SZ, _P]),
@@ -296,6 +300,35 @@ def w12_lmhead_argmax(mat: W12Matrix, x, idx, max_logit, ws, stream=None):
                                    _ptr(ws), ws.numel(), _stream(stream)), "w12_lmhead_argmax")
 
 
+def w12_certify_bounds(mat: W12Matrix, bounds: torch.Tensor, stream=None):
+    _on(mat, bounds, "bounds")
+    if bounds.dtype != torch.float32 or bounds.numel() < 2 * mat.n or not bounds.is_contiguous():
+        raise ValueError(f"bounds must be a contiguous float32 tensor of 2 * {mat.n} entries")
+    d = mat.desc()
+    _check(lib().w12_certify_bounds(ctypes.byref(d), _ptr(bounds), _stream(stream)), "w12_certify_bounds")
+
+
+def w12_lmhead_argmax_certified(mat: W12Matrix, bounds, x, idx, max_logit, survivors, ws, stream=None):
+    _check_x(mat, x)
+    m = x.shape[0]
+    for t, name, dt in ((idx, "idx", torch.int32), (max_logit, "max_logit", torch.float32),
+                        (survivors, "survivors", torch.int32)):
+        if t is None and name == "idx":
+            raise ValueError("idx is required")
+        if t is not None:
+            _on(mat, t, name)
+            if t.dtype != dt or t.numel() < m or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {dt} tensor of M entries")
+    _on(mat, bounds, "bounds")
+    if bounds.dtype != torch.float32 or bounds.numel() < 2 * mat.n:
+        raise ValueError("bounds must come from w12_certify_bounds (float32, 2 N entries)")
+    _check_ws(mat, ws)
+    d = mat.desc()
+    _check(lib().w12_lmhead_argmax_certified(ctypes.byref(d), _ptr(bounds), _ptr(x), m, x.stride(0), _ptr(idx),
+                                             _ptr(max_logit), _ptr(survivors), _ptr(ws), ws.numel(),
+                                             _stream(stream)), "w12_lmhead_argmax_certified")
+
+
 def w12_validate(mat: W12Matrix, ws: torch.Tensor, stream=None) -> int:
     _check_ws(mat, ws)
     d = mat.desc()
@@ -366,3 +399,22 @@ def lmhead_argmax(mat: W12Matrix, x: torch.Tensor, stream=None):
     ws, _ = _workspace(OP_LMHEAD_ARGMAX, mat.n, mat.k, m, mat.device)
     w12_lmhead_argmax(mat, x, idx, mx, ws, stream)
     return idx, mx
+
+
+def certify_bounds(mat: W12Matrix, stream=None) -> torch.Tensor:
+    """Per-row bounds [N, 2] (r_n, a_n) of the certified LM head."""
+    b = torch.empty((mat.n, 2), dtype=torch.float32, device=mat.device)
+    w12_certify_bounds(mat, b, stream)
+    return b
+
+
+def lmhead_argmax_certified(mat: W12Matrix, bounds: torch.Tensor, x: torch.Tensor, stream=None):
+    """(idx, max_logit, survivors) of the certified argmax LM head."""
+    x = _as_bits16(x)
+    m = x.shape[0]
+    idx = torch.empty(m, dtype=torch.int32, device=mat.device)
+    mx = torch.empty(m, dtype=torch.float32, device=mat.device)
+    sv = torch.empty(m, dtype=torch.int32, device=mat.device)
+    ws, _ = _workspace(OP_LMHEAD_CERTIFIED, mat.n, mat.k, m, mat.device)
+    w12_lmhead_argmax_certified(mat, bounds, x, idx, mx, sv, ws, stream)
+    return idx, mx, sv

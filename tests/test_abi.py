@@ -255,3 +255,23 @@ def test_noalloc_refuses_shapes_beyond_its_scratch():
     assert lib.w12_gemm_noalloc(ctypes.byref(m), FAKE, 0, 1024, FAKE, 1024, w12.F32, None) == w12.E_M_RANGE
     assert lib.w12_gemm_noalloc(ctypes.byref(m), FAKE, 4, 1000, FAKE, 1024, w12.F32, None) == w12.E_INVALID_ARG
     assert lib.w12_gemm_noalloc(None, FAKE, 4, 1024, FAKE, 1024, w12.F32, None) == w12.E_INVALID_ARG
+
+
+def test_certified_head_argument_errors():
+    """The certified LM head checks its arguments and workspace before any HIP
+    call (fake pointers: nothing may be launched)."""
+    lib = w12.lib()
+    m = w12.MatrixC(151936, 5120, FAKE, FAKE, FAKE, 0, 0, w12.FORMAT_VERSION)
+    need = w12.workspace_bytes(w12.OP_LMHEAD_CERTIFIED, 151936, 5120, 32)
+    assert need > 32 * 151936 * 4                       # holds the Q logits
+    assert need >= w12.workspace_bytes(w12.OP_LMHEAD_ARGMAX, 151936, 5120, 32)
+    call = lambda b, mm, ws_bytes: lib.w12_lmhead_argmax_certified(  # noqa: E731
+        ctypes.byref(m), b, FAKE, mm, 5120, FAKE, None, None, FAKE, ws_bytes, None)
+    assert call(FAKE, 32, need - 1) == w12.E_WORKSPACE
+    assert call(None, 32, need) == w12.E_INVALID_ARG
+    assert call(FAKE, 0, need) == w12.E_M_RANGE
+    assert call(FAKE, 65, need) == w12.E_M_RANGE
+    assert lib.w12_certify_bounds(ctypes.byref(m), None, None) == w12.E_INVALID_ARG
+    assert lib.w12_certify_bounds(ctypes.byref(m), FAKE + 4, None) == w12.E_INVALID_ARG
+    bad = w12.MatrixC(151936, 5120, FAKE, FAKE, FAKE, 0, 0, 99)
+    assert lib.w12_certify_bounds(ctypes.byref(bad), FAKE, None) == w12.E_VERSION
