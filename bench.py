@@ -364,6 +364,7 @@ def workloads(torch, w12, synth, dev, stream, reps):
         uqe = time_shape(torch, w12, stream, mats, x, y, ws, max(4, reps // 2), op="q8", q_flags=w12.Q8_APPLY_ESCAPES)
         out[tag] = {"n": spec.n, "k": spec.k, "n_esc": mat.n_esc,
                     "exact_us": round(ue, 2), "exact_kernel": w12.plan_info(mat, w12.OP_GEMM, 32)["kernel_name"],
+                    "exact_fixup_kernel": bool(w12.plan_info(mat, w12.OP_GEMM, 32)["fixup"]),
                     "q_view_us": round(uq, 2), "q_view_gbs": round(spec.n * spec.k / uq / 1e3, 1),
                     "q_view_escapes_us": round(uqe, 2),
                     "q_kernel": w12.plan_info(mat, w12.OP_GEMM_Q8, 32)["kernel_name"]}

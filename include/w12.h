@@ -265,7 +265,8 @@ typedef struct {
   int32_t unit_cols;       /* columns of a stream-K unit                               */
   int64_t split_units;     /* units of the split tiles                                 */
   int32_t prepass;         /* 1: an activation transpose kernel runs before the GEMM   */
-  int32_t reserved;
+  int32_t fixup;           /* 1: dense escapes: the GEMM runs without escape work and  */
+                           /*    a fix-up kernel applies the escapes after it          */
   size_t workspace_bytes;  /* what this plan uses (w12_workspace_bytes covers them all) */
 } w12_plan;
 
@@ -279,7 +280,9 @@ int w12_plan_info(const w12_matrix* m, int op, int64_t M, uint32_t flags, w12_pl
 /* Test hooks, per calling thread (other threads' calls are unaffected).
  * W12_TUNE_PATH: 0 = the library's choice, 1 = the GEMV kernel (M <= 16),
  *   2 = the MFMA helper-wave kernel, 3 = the MFMA stream kernel (where it
- *   applies; the fused argmax always runs the helper-wave kernel).
+ *   applies; the fused argmax always runs the helper-wave kernel), 4 = the
+ *   dense-escape path (GEMM without escape work, then the fix-up kernel) for
+ *   any matrix with escapes (the library's choice above 8 escapes per row).
  * W12_TUNE_GRID: workgroup count for the GEMM kernels (0 = the library's
  *   choice: 256, or c * T for a matrix of T < 256 tiles; at most 4096 and at
  *   most the number of work units are used).

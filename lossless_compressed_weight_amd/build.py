@@ -16,7 +16,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libw12.so")
-SOURCES = ["w12_gemm.hip", "w12_gemm_mx.hip", "w12_api.hip", "w12_encode.hip", "w12_certify.hip", "w12_probe.hip"]
+# The same library with AddressSanitizer and UndefinedBehaviorSanitizer in the
+# host code of the C ABI (argument checks, sizes, plans, dispatch); its device
+# code is the normal build. Loaded only by the host-side check in tests/host.
+HOSTCHECK_LIB = os.path.join(PKG, "libw12_hostcheck.so")
+HOST_SANITIZE = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined -Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer -Xarch_host -g".split()
+HOSTCHECK_SOURCE = "w12_api.hip"
+SOURCES = ["w12_gemm.hip", "w12_gemm_mx.hip", "w12_api.hip", "w12_encode.hip", "w12_certify.hip", "w12_fixup.hip", "w12_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -58,14 +64,30 @@ def build(verbose: bool = False) -> str:
                 raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
             return obj
 
+        def compile_hostcheck():
+            obj = os.path.join(tmp, "hostcheck_" + HOSTCHECK_SOURCE.replace(".hip", ".o"))
+            cmd = [cc, *HIPCC_FLAGS, *HOST_SANITIZE, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+                   os.path.join(CSRC, HOSTCHECK_SOURCE), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc (host sanitizers) failed on {HOSTCHECK_SOURCE}:\n{r.stdout}\n{r.stderr}")
+            return obj
+
         with ThreadPoolExecutor(_jobs()) as ex:
+            check_obj = ex.submit(compile_hostcheck)
             objs = list(ex.map(compile_one, SOURCES))
-        tmp_lib = LIB + ".tmp"
-        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-        os.replace(tmp_lib, LIB)
+            check_obj = check_obj.result()
+
+        def link(objects, out):
+            tmp_lib = out + ".tmp"
+            cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objects, "-o", tmp_lib]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+            os.replace(tmp_lib, out)
+        link(objs, LIB)
+        link([check_obj if os.path.basename(o) == HOSTCHECK_SOURCE.replace(".hip", ".o") else o for o in objs],
+             HOSTCHECK_LIB)
     return LIB
 
 

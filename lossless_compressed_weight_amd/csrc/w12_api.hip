@@ -82,7 +82,19 @@ size_t gemm_ws_bytes(const GemmPlan& pl) {
 size_t mx_ws_bytes(const MxPlan& pl) { return round256(kCounterBytes) + round256(pl.part_bytes); }
 
 GemmPlan make_plan(int64_t n, int64_t k, int64_t M, int op) {
-  return plan_gemm(n, k, M, op, g_tune_path == 3 ? 2 : g_tune_path, g_tune_grid);
+  return plan_gemm(n, k, M, op, g_tune_path == 3 ? 2 : (g_tune_path == 4 ? 0 : g_tune_path), g_tune_grid);
+}
+
+// Matrices with more escapes than this per row on average (the escape-stress
+// workload has about 55, the normal ones about 1.4) take the dense path: the
+// GEMM without escape work, then the fix-up kernel (w12_fixup.hip) with every
+// lane busy, instead of the per-segment fix-up on one helper wave per CU.
+constexpr int64_t kDenseEscPerRow = 8;
+
+bool dense_path(const w12_matrix* m, int op, bool fix) {
+  if (!fix || op == W12_OP_LMHEAD_ARGMAX || m->n_esc == 0) return false;
+  if (g_tune_path == 4) return true;
+  return g_tune_path == 0 && m->n_esc > kDenseEscPerRow * m->n;
 }
 
 // The kernel a call runs: the lane-per-row GEMV for M <= 2; from M = 3 an
@@ -96,6 +108,7 @@ GemmPlan make_plan(int64_t n, int64_t k, int64_t M, int op) {
 // 5120 x 17408 37.4 vs 37.5, 17408 x 5120 37.3 vs 32.2 (stream vs helper).
 int choose_kernel(int64_t n, int64_t k, int64_t n_esc, int64_t M, int op, bool fix, const GemmPlan& old) {
   const bool mx_ok = op != W12_OP_LMHEAD_ARGMAX && k <= kMxMaxK;
+  if (g_tune_path == 4) fix = false;  // the dense path runs its GEMM without escape work
   if (g_tune_path == 1) return W12_KERNEL_GEMV;
   if (g_tune_path == 2) return W12_KERNEL_MFMA_HELPER;
   if (g_tune_path == 3) return mx_ok ? W12_KERNEL_MFMA_STREAM : W12_KERNEL_MFMA_HELPER;
@@ -124,14 +137,33 @@ CertLayout cert_layout(int64_t n, int64_t k, int64_t M) {
   return c;
 }
 
-// Every plan a GEMM op may run for this shape fits in this much workspace.
-size_t ws_bytes_any(int64_t n, int64_t k, int64_t M, int op) {
+// Every GEMM kernel plan for this shape fits in this much workspace.
+size_t ws_bytes_kernels(int64_t n, int64_t k, int64_t M, int op) {
   size_t b = gemm_ws_bytes(make_plan(n, k, M, op));
   if (op != W12_OP_LMHEAD_ARGMAX && k <= kMxMaxK) {
     const size_t bx = mx_ws_bytes(plan_mx(n, k, M, g_tune_grid));
     if (bx > b) b = bx;
   }
   return b;
+}
+
+// The dense path's workspace: [kernel plans | fp32 sums [M][N] | xT [K][mm]].
+struct DenseLayout {
+  size_t main, a, xt, total;
+};
+DenseLayout dense_layout(int64_t n, int64_t k, int64_t M, int op) {
+  DenseLayout d{};
+  d.main = round256(ws_bytes_kernels(n, k, M, op));
+  d.a = d.main;
+  d.xt = d.a + round256((size_t)M * (size_t)n * sizeof(float));
+  d.total = d.xt + round256((size_t)k * (size_t)(((M + 15) / 16) * 16) * sizeof(uint16_t));
+  return d;
+}
+
+// Every path a GEMM op may take for this shape fits in this much workspace.
+size_t ws_bytes_any(int64_t n, int64_t k, int64_t M, int op) {
+  if (op == W12_OP_LMHEAD_ARGMAX) return ws_bytes_kernels(n, k, M, op);
+  return dense_layout(n, k, M, op).total;
 }
 
 int run_mx(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
@@ -163,11 +195,49 @@ int run_mx(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void*
   return W12_OK;
 }
 
+int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
+             int op, bool fix, void* ws, size_t ws_bytes, int32_t* idx, float* maxv, void* stream,
+             const uint32_t* gate = nullptr);
+
+// Dense escapes: activations transposed for the fix-up, the GEMM without escape
+// work into fp32 sums, then the fix-up kernel writes y.
+int run_dense(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
+              int op, void* ws, size_t ws_bytes, void* stream) {
+  const DenseLayout d = dense_layout(m->n, m->k, M, op);
+  if (!ws || ws_bytes < d.total) return W12_E_WORKSPACE;
+  char* wsb = reinterpret_cast<char*>(ws);
+  float* a = reinterpret_cast<float*>(wsb + d.a);
+  uint16_t* xt = reinterpret_cast<uint16_t*>(wsb + d.xt);
+  const int mm = (int)(((M + 15) / 16) * 16);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_xpose(x, ldx, (int)M, mm, (int)m->k, xt, nullptr, nullptr, st);
+  if (e != hipSuccess) return hip_fail(e, "dense escapes: activation transpose launch");
+  const int r = run_gemm(m, x, M, ldx, a, m->n, W12_F32, op, false, ws, d.main, nullptr, nullptr, stream);
+  if (r != W12_OK) return r;
+  FixParams p{};
+  p.a = a;
+  p.row_ptr = m->esc_row_ptr;
+  p.esc = reinterpret_cast<const uint2*>(m->esc);
+  p.xt = xt;
+  p.y = y;
+  p.ldy = ldy;
+  p.n = (int)m->n;
+  p.m = (int)M;
+  p.mm = mm;
+  p.y_f32 = y_dtype == W12_F32;
+  p.q = op == W12_OP_GEMM_Q8;
+  p.slices = fix_slices(m->n, m->n_esc, (int)M);
+  e = launch_fix_dense(p, st);
+  if (e != hipSuccess) return hip_fail(e, "dense escapes: fix-up launch");
+  return W12_OK;
+}
+
 // gate: null, or a device word that a kernel on the stream writes before this
 // call's kernels run; they do nothing when it is zero (helper-wave kernels only).
 int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
              int op, bool fix, void* ws, size_t ws_bytes, int32_t* idx, float* maxv, void* stream,
-             const uint32_t* gate = nullptr) {
+             const uint32_t* gate) {
+  if (!gate && dense_path(m, op, fix)) return run_dense(m, x, M, ldx, y, ldy, y_dtype, op, ws, ws_bytes, stream);
   const GemmPlan pl = make_plan(m->n, m->k, M, op);
   const int kernel = gate ? (pl.mfma ? W12_KERNEL_MFMA_HELPER : W12_KERNEL_GEMV)
                           : choose_kernel(m->n, m->k, m->n_esc, M, op, fix, pl);
@@ -317,7 +387,9 @@ int w12_plan_info(const w12_matrix* m, int op, int64_t M, uint32_t flags, w12_pl
   if (op != W12_OP_GEMM && op != W12_OP_GEMM_Q8 && op != W12_OP_LMHEAD_ARGMAX) return W12_E_INVALID_ARG;
   if (M < 1 || M > W12_MAX_M) return W12_E_M_RANGE;
   if (flags & ~W12_Q8_APPLY_ESCAPES) return W12_E_INVALID_ARG;
-  const bool fix = op != W12_OP_GEMM_Q8 || (flags & W12_Q8_APPLY_ESCAPES);
+  bool fix = op != W12_OP_GEMM_Q8 || (flags & W12_Q8_APPLY_ESCAPES);
+  const bool dense = dense_path(m, op, fix);
+  if (dense) fix = false;
   const GemmPlan pl = make_plan(m->n, m->k, M, op);
   w12_plan o{};
   o.kernel = choose_kernel(m->n, m->k, m->n_esc, M, op, fix, pl);
@@ -345,6 +417,11 @@ int w12_plan_info(const w12_matrix* m, int op, int64_t M, uint32_t flags, w12_pl
     o.split_units = pl.sk_units;
     o.prepass = pl.mfma ? 1 : 0;
     o.workspace_bytes = gemm_ws_bytes(pl);
+  }
+  if (dense) {
+    o.fixup = 1;
+    o.prepass = 1;
+    o.workspace_bytes = dense_layout(m->n, m->k, M, op).total;
   }
   *out = o;
   return W12_OK;

@@ -216,6 +216,24 @@ struct GemmPlan {
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int op, int path, int64_t grid_override);
 hipError_t launch_gemm(const GemmPlan& plan, GemmParams p, hipStream_t s, int* unsupported);
 
+// ------------------------------------------------------------------ dense escapes
+// The escape fix-up as a kernel of its own after a GEMM run without escape
+// work (w12_fixup.hip): y = (a - CN) + CP per output.
+struct FixParams {
+  const float* a;            // fp32 sums with the placeholders in place [M][N] (row stride N)
+  const uint32_t* row_ptr;
+  const uint2* esc;
+  const uint16_t* xt;        // activations transposed [K][mm], rows past M zero
+  void* y;
+  int64_t ldy;
+  int n, m, mm;
+  int y_f32;
+  int q;                     // Q pass: the placeholder term uses the placeholder's view
+  int slices;                // groups per output row (fix_slices)
+};
+int fix_slices(int64_t n, int64_t n_esc, int m);
+hipError_t launch_fix_dense(const FixParams& p, hipStream_t s);
+
 // ------------------------------------------------------------------ certified LM head
 // Per-call state of the certified head (w12_certify.hip), in the workspace;
 // zero before a workspace's first use and cleared again by every call (the

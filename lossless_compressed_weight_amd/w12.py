@@ -34,6 +34,7 @@ OP_ENCODE_PLAN, OP_GEMM, OP_GEMM_Q8, OP_LMHEAD_ARGMAX, OP_LMHEAD_CERTIFIED = 1, 
 CERT_MAX_SURVIVORS = 256
 Q8_APPLY_ESCAPES = 1
 TUNE_PATH, TUNE_GRID = 1, 2
+PATH_DENSE = 4          # W12_TUNE_PATH value forcing the dense-escape path
 KERNEL_GEMV, KERNEL_MFMA_HELPER, KERNEL_MFMA_STREAM = 1, 2, 3
 KERNEL_NAMES = {KERNEL_GEMV: "gemv", KERNEL_MFMA_HELPER: "mfma_helper", KERNEL_MFMA_STREAM: "mfma_stream"}
 
@@ -61,7 +62,7 @@ class PlanC(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("grid", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("tile_rows", ctypes.c_int32), ("whole_tiles", ctypes.c_int32), ("split_tiles", ctypes.c_int32),
                 ("split_tile_rows", ctypes.c_int32), ("unit_cols", ctypes.c_int32), ("split_units", ctypes.c_int64),
-                ("prepass", ctypes.c_int32), ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+                ("prepass", ctypes.c_int32), ("fixup", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
 
 
 _P = ctypes.c_void_p
@@ -147,7 +148,7 @@ def plan_info(mat_or_desc, op: int, m: int, flags: int = 0) -> dict:
     d = mat_or_desc.desc() if hasattr(mat_or_desc, "desc") else mat_or_desc
     out = PlanC()
     _check(lib().w12_plan_info(ctypes.byref(d), op, m, flags, ctypes.byref(out)), "w12_plan_info")
-    rec = {f: getattr(out, f) for f, _ in PlanC._fields_ if f != "reserved"}
+    rec = {f: getattr(out, f) for f, _ in PlanC._fields_}
     rec["kernel_name"] = KERNEL_NAMES.get(out.kernel, "?")
     return rec
 

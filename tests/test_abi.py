@@ -159,12 +159,15 @@ def test_plan_arithmetic(n, k, m):
             units = -(-n // plan["tile_rows"]) * (k // plan["unit_cols"])
             assert plan["grid"] <= units
             _plan_covers_rows(plan, n)
-            if op == w12.OP_LMHEAD_ARGMAX or (n_esc > 8 * n and op != w12.OP_GEMM_Q8):
+            # dense escapes: the GEMM runs without escape work, a fix-up kernel follows
+            dense = n_esc > 8 * n and op == w12.OP_GEMM
+            assert plan["fixup"] == int(dense)
+            if op == w12.OP_LMHEAD_ARGMAX:
                 assert plan["kernel"] in (w12.KERNEL_GEMV, w12.KERNEL_MFMA_HELPER)
             if m <= 2:
                 assert plan["kernel"] == w12.KERNEL_GEMV
-            elif -(-(n // 16) // 4) < 256 and m <= 32 and op != w12.OP_LMHEAD_ARGMAX and (n_esc <= 8 * n or op == w12.OP_GEMM_Q8):
-                assert plan["kernel"] == w12.KERNEL_MFMA_STREAM and plan["prepass"] == 0
+            elif -(-(n // 16) // 4) < 256 and m <= 32 and op != w12.OP_LMHEAD_ARGMAX:
+                assert plan["kernel"] == w12.KERNEL_MFMA_STREAM and plan["prepass"] == int(dense)
             else:
                 assert plan["kernel"] == w12.KERNEL_MFMA_HELPER
 
