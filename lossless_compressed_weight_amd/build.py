@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libw12.so")
 HOSTCHECK_LIB = os.path.join(PKG, "libw12_hostcheck.so")
 HOST_SANITIZE = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined -Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer -Xarch_host -g".split()
 HOSTCHECK_SOURCE = "w12_api.hip"
-SOURCES = ["w12_gemm.hip", "w12_gemm_mx.hip", "w12_api.hip", "w12_encode.hip", "w12_certify.hip", "w12_fixup.hip", "w12_probe.hip"]
+SOURCES = ["w12_gemm.hip", "w12_gemm_mx.hip", "w12_api.hip", "w12_encode.hip", "w12_certify.hip", "w12_fixup.hip", "w12_argmax.hip", "w12_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -160,9 +160,25 @@ DenseLayout dense_layout(int64_t n, int64_t k, int64_t M, int op) {
   return d;
 }
 
+// The two-pass argmax's workspace: [kernel plans of both ops | fp32 logits [M][N] | keys | counters], one
+// 256-byte line of keys and one of counters per activation row.
+struct ArgmaxLayout {
+  size_t main, logits, keys, ctr, total;
+};
+ArgmaxLayout argmax_layout(int64_t n, int64_t k, int64_t M) {
+  ArgmaxLayout L{};
+  L.main = round256(std::max(ws_bytes_kernels(n, k, M, W12_OP_GEMM), ws_bytes_kernels(n, k, M, W12_OP_LMHEAD_ARGMAX)));
+  L.logits = L.main;
+  L.keys = L.logits + round256((size_t)M * (size_t)n * sizeof(float));
+  L.ctr = L.keys + (size_t)W12_MAX_M * kArgmaxStateBytes;
+  L.total = L.ctr + (size_t)W12_MAX_M * kArgmaxStateBytes;
+  return L;
+}
+
 // Every path a GEMM op may take for this shape fits in this much workspace.
 size_t ws_bytes_any(int64_t n, int64_t k, int64_t M, int op) {
-  if (op == W12_OP_LMHEAD_ARGMAX) return ws_bytes_kernels(n, k, M, op);
+  if (op == W12_OP_LMHEAD_ARGMAX)
+    return M > kFusedArgmaxMaxM ? argmax_layout(n, k, M).total : ws_bytes_kernels(n, k, M, op);
   return dense_layout(n, k, M, op).total;
 }
 
@@ -197,7 +213,7 @@ int run_mx(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void*
 
 int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
              int op, bool fix, void* ws, size_t ws_bytes, int32_t* idx, float* maxv, void* stream,
-             const uint32_t* gate = nullptr);
+             const uint32_t* gate = nullptr, int force_kernel = 0);
 
 // Dense escapes: activations transposed for the fix-up, the GEMM without escape
 // work into fp32 sums, then the fix-up kernel writes y.
@@ -232,15 +248,40 @@ int run_dense(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, vo
   return W12_OK;
 }
 
+// The LM-head argmax above 16 activation rows, in two passes: the helper-wave
+// kernel stores the fp32 logits (the same kernel and summation order as the
+// fused argmax, so the same values), then k_rows_argmax folds each row.
+int run_argmax_two_pass(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, bool fix, void* ws,
+                        size_t ws_bytes, int32_t* idx, float* maxv, void* stream, const uint32_t* gate) {
+  const ArgmaxLayout L = argmax_layout(m->n, m->k, M);
+  if (!ws || ws_bytes < L.total) return W12_E_WORKSPACE;
+  char* wsb = reinterpret_cast<char*>(ws);
+  float* logits = reinterpret_cast<float*>(wsb + L.logits);
+  const int r = run_gemm(m, x, M, ldx, logits, m->n, W12_F32, W12_OP_GEMM, fix, ws, L.main, nullptr, nullptr, stream,
+                         gate, W12_KERNEL_MFMA_HELPER);
+  if (r != W12_OK) return r;
+  const hipError_t e = launch_rows_argmax(logits, m->n, (int)m->n, (int)M,
+                                          reinterpret_cast<unsigned long long*>(wsb + L.keys),
+                                          reinterpret_cast<uint32_t*>(wsb + L.ctr), idx, maxv, gate,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "argmax of the stored logits: launch");
+  return W12_OK;
+}
+
 // gate: null, or a device word that a kernel on the stream writes before this
 // call's kernels run; they do nothing when it is zero (helper-wave kernels only).
+// force_kernel: 0, or the kernel to run whatever the usual choice.
 int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
              int op, bool fix, void* ws, size_t ws_bytes, int32_t* idx, float* maxv, void* stream,
-             const uint32_t* gate) {
-  if (!gate && dense_path(m, op, fix)) return run_dense(m, x, M, ldx, y, ldy, y_dtype, op, ws, ws_bytes, stream);
+             const uint32_t* gate, int force_kernel) {
+  if (op == W12_OP_LMHEAD_ARGMAX && M > kFusedArgmaxMaxM)
+    return run_argmax_two_pass(m, x, M, ldx, fix, ws, ws_bytes, idx, maxv, stream, gate);
+  if (!gate && !force_kernel && dense_path(m, op, fix))
+    return run_dense(m, x, M, ldx, y, ldy, y_dtype, op, ws, ws_bytes, stream);
   const GemmPlan pl = make_plan(m->n, m->k, M, op);
-  const int kernel = gate ? (pl.mfma ? W12_KERNEL_MFMA_HELPER : W12_KERNEL_GEMV)
-                          : choose_kernel(m->n, m->k, m->n_esc, M, op, fix, pl);
+  const int kernel = force_kernel ? force_kernel
+                     : gate     ? (pl.mfma ? W12_KERNEL_MFMA_HELPER : W12_KERNEL_GEMV)
+                                : choose_kernel(m->n, m->k, m->n_esc, M, op, fix, pl);
   if (kernel == W12_KERNEL_MFMA_STREAM) return run_mx(m, x, M, ldx, y, ldy, y_dtype, op, fix, ws, ws_bytes, stream);
   if (!pl.mfma && M > 16) return W12_E_M_RANGE;
   const size_t need = gemm_ws_bytes(pl);
@@ -423,6 +464,7 @@ int w12_plan_info(const w12_matrix* m, int op, int64_t M, uint32_t flags, w12_pl
     o.prepass = 1;
     o.workspace_bytes = dense_layout(m->n, m->k, M, op).total;
   }
+  if (op == W12_OP_LMHEAD_ARGMAX && M > kFusedArgmaxMaxM) o.workspace_bytes = argmax_layout(m->n, m->k, M).total;
   *out = o;
   return W12_OK;
 }

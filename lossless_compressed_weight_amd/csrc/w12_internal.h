@@ -234,6 +234,16 @@ struct FixParams {
 int fix_slices(int64_t n, int64_t n_esc, int m);
 hipError_t launch_fix_dense(const FixParams& p, hipStream_t s);
 
+// ------------------------------------------------------------------ argmax of stored logits
+// The LM-head argmax above 16 activation rows: the GEMM stores fp32 logits,
+// then this kernel folds each row (w12_argmax.hip). keys and ctr hold one
+// 256-byte line per activation row (kArgmaxStateBytes), zero before the call;
+// the last workgroup of each row clears its line again.
+constexpr size_t kArgmaxStateBytes = 256;
+constexpr int kFusedArgmaxMaxM = 16;  // the fused argmax keeps its per-lane fold up to here
+hipError_t launch_rows_argmax(const float* y, int64_t ldy, int n, int M, unsigned long long* keys, uint32_t* ctr,
+                              int32_t* idx, float* maxv, const uint32_t* gate, hipStream_t s);
+
 // ------------------------------------------------------------------ certified LM head
 // Per-call state of the certified head (w12_certify.hip), in the workspace;
 // zero before a workspace's first use and cleared again by every call (the
