@@ -22,12 +22,11 @@
 //                  largest lower bound (atomic max per activation row) and its
 //                  largest upper bound (kept per chunk)
 //   k_cert_select  chunks whose largest upper bound reaches the best lower
-//                  bound list their surviving rows; a row count past the cap
-//                  raises the fallback flag
+//                  bound list their surviving rows
 //   k_cert_rescore one wave per (activation row, survivor): exact dot product
-//                  from the record bytes and the escape list, 64-bit argmax key
-//   k_cert_final   indices and maxima from the keys (unless the flag is up),
-//                  survivor counts, and the state cleared for the next call
+//                  from the record bytes and the escape list, 64-bit argmax
+//                  key; the row's last pair writes its index and maximum. A row
+//                  past the cap raises the gate instead.
 // The full fused head then runs gated on the flag.
 #include "w12_internal.h"
 
@@ -167,6 +166,8 @@ __device__ double row_norm(const uint16_t* x, int k, double* red) {
   return sqrt(t);
 }
 
+// Per (chunk of rows, activation row m): ||x_m||, the chunk's largest lower
+// bound (atomic max per activation row) and its largest upper bound.
 __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
   __shared__ double red[kCertThreads / 64];
   __shared__ float lo_w[kCertThreads / 64], hi_w[kCertThreads / 64];
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
   const double xn = row_norm(a.x + (int64_t)m * a.ldx, a.k, red);
   if (chunk == 0 && threadIdx.x == 0) {
     a.st->xnorm[m] = xn;
-    if (m == 0) a.st->flag = 0u;  // raised again by k_cert_select if needed
+    a.st->count[m] = 0u;  // the survivors are counted by k_cert_select
   }
   float lo = -__builtin_inff(), hi = -__builtin_inff();
   const int r0 = chunk * kCertChunk;
@@ -204,13 +205,13 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
       lo = fmaxf(lo, lo_w[w]);
       hi = fmaxf(hi, hi_w[w]);
     }
-    lo = fmaxf(lo, lo_w[0]);
-    hi = fmaxf(hi, hi_w[0]);
     __hip_atomic_fetch_max(&a.st->lower[m], ord32(lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     a.ub_chunk[(int64_t)m * a.chunks + chunk] = hi;
   }
 }
 
+// Chunks whose largest upper bound reaches the best lower bound list their
+// surviving rows (the count may pass the cap; entries past it are dropped).
 __global__ __launch_bounds__(kCertThreads) void k_cert_select(CertArgs a) {
   const int chunk = blockIdx.x, m = blockIdx.y;
   const float best_lower = unord32(a.st->lower[m]);
@@ -237,8 +238,6 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_select(CertArgs a) {
       const uint32_t pos = pos0 + (uint32_t)__popcll(ballot & ((1ull << lane) - 1ull));
       if (pos < (uint32_t)a.cap) a.list[(int64_t)m * a.cap + pos] = (uint32_t)row;
     }
-    if (lane == 0 && pos0 + (uint32_t)__popcll(ballot) > (uint32_t)a.cap)
-      __hip_atomic_fetch_or(&a.st->flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -251,20 +250,41 @@ struct RescoreArgs {
   int64_t ldx;
   CertState* st;
   const uint32_t* list;
+  int32_t* idx;
+  float* maxv;
+  int32_t* survivors;
   int n, k, m, cap;
 };
 
+__device__ __forceinline__ int32_t sat_i32(uint32_t c) { return c > 0x7FFFFFFFu ? 0x7FFFFFFF : (int32_t)c; }
+
 // One wave per (activation row, surviving row), waves striding over the
-// flattened list. The dot product runs over the exact decode (placeholders at
+// flattened lists. The dot product runs over the exact decode (placeholders at
 // escapes), then each escape adds x * (exact - placeholder); both in fp32 in a
-// fixed order, so a pair's logit does not depend on the schedule.
+// fixed order, so a pair's logit does not depend on the schedule. The last of
+// row m's pairs to finish writes idx[m] and max_logit[m]. When any row kept
+// more than the cap, nothing is rescored: the full head's gate goes up.
 __global__ __launch_bounds__(kCertThreads) void k_cert_rescore(RescoreArgs a) {
   const int lane = threadIdx.x & 63;
-  if (__hip_atomic_load(&a.st->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
   // per-activation-row counts and their inclusive prefix (lane = row)
   uint32_t c = 0;
-  if (lane < a.m) c = __hip_atomic_load(&a.st->count[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (c > (uint32_t)a.cap) c = (uint32_t)a.cap;  // (the flag is up then; kept for safety)
+  if (lane < a.m) c = a.st->count[lane];
+  const bool fallback = __ballot(c > (uint32_t)a.cap) != 0ull;
+  if (blockIdx.x == 0 && threadIdx.x < 64) {
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&a.st->flag, fallback ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane < kCertMaxM) a.st->lower[lane] = 0u;  // read by no kernel after k_cert_select
+    if (lane < a.m && (fallback || c == 0u)) {
+      // the full head answers (or, with no survivor at all, which the bounds
+      // rule out, index 0): only the counts are reported here
+      if (a.survivors) a.survivors[lane] = sat_i32(c);
+      if (!fallback) {
+        a.idx[lane] = 0;
+        if (a.maxv) a.maxv[lane] = -__builtin_inff();
+      }
+    }
+  }
+  if (fallback) return;
   uint32_t incl = c;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -278,6 +298,7 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_rescore(RescoreArgs a) {
   for (uint32_t t = blockIdx.x * (kCertThreads / 64) + (threadIdx.x >> 6); t < total; t += (uint32_t)waves) {
     const uint64_t past = __ballot(incl > t);           // rows whose prefix passes t
     const int m = __builtin_ctzll(past);
+    const uint32_t cm = __shfl(c, m, 64);
     const uint32_t excl = __shfl(incl - c, m, 64);
     const uint32_t row = a.list[(int64_t)m * a.cap + (t - excl)];
     const int r = row & 15;
@@ -286,19 +307,35 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_rescore(RescoreArgs a) {
     const uint32_t bias2 = bias | (bias << 16);
     const uint16_t* xr = a.x + (int64_t)m * a.ldx;
     float acc = 0.f;
-    for (int kb = lane >> 5; kb < kb_count; kb += 2) {
-      const uint8_t* rp = blk + (int64_t)kb * kRecBytes;
-      const uint4 v = *reinterpret_cast<const uint4*>(rp + (G * 16 + r) * 16);
-      const uint2 b = *reinterpret_cast<const uint2*>(rp + kViewBytes + (G * 16 + r) * 8);
-      const uint4* xp = reinterpret_cast<const uint4*>(xr + kb * kRecCols + G * 16);
-      const uint4 x0 = xp[0], x1 = xp[1];
-      const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      uint32_t d[8];
-      decode16_exact(v, b, d, bias2);
+    // records kb = lane / 32 + 2 i, four at a time with every load issued first
+    constexpr int kRB = 4;
+    for (int kb0 = lane >> 5; kb0 < kb_count; kb0 += 2 * kRB) {
+      uint4 v[kRB], x0[kRB], x1[kRB];
+      uint2 b[kRB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        acc = fmaf(bf16_to_f32(d[j] & 0xFFFFu), bf16_to_f32(xw[j] & 0xFFFFu), acc);
-        acc = fmaf(bf16_to_f32(d[j] >> 16), bf16_to_f32(xw[j] >> 16), acc);
+      for (int i = 0; i < kRB; ++i) {
+        const int kb = kb0 + 2 * i;
+        if (kb < kb_count) {
+          const uint8_t* rp = blk + (int64_t)kb * kRecBytes;
+          v[i] = *reinterpret_cast<const uint4*>(rp + (G * 16 + r) * 16);
+          b[i] = *reinterpret_cast<const uint2*>(rp + kViewBytes + (G * 16 + r) * 8);
+          const uint4* xp = reinterpret_cast<const uint4*>(xr + kb * kRecCols + G * 16);
+          x0[i] = xp[0];
+          x1[i] = xp[1];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) {
+        if (kb0 + 2 * i < kb_count) {
+          const uint32_t xw[8] = {x0[i].x, x0[i].y, x0[i].z, x0[i].w, x1[i].x, x1[i].y, x1[i].z, x1[i].w};
+          uint32_t d[8];
+          decode16_exact(v[i], b[i], d, bias2);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            acc = fmaf(bf16_to_f32(d[j] & 0xFFFFu), bf16_to_f32(xw[j] & 0xFFFFu), acc);
+            acc = fmaf(bf16_to_f32(d[j] >> 16), bf16_to_f32(xw[j] >> 16), acc);
+          }
+        }
       }
     }
     float corr = 0.f;
@@ -310,31 +347,21 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_rescore(RescoreArgs a) {
       corr = fmaf(-xv, bf16_to_f32(e.y >> 16), corr);
     }
     const float logit = wave_sum_f32(acc) + wave_sum_f32(corr);
-    if (lane == 0)
+    if (lane == 0) {
+      // the key and the count are atomics at the coherence point; the count
+      // goes in only once the key has, so the row's last pair reads them all
       __hip_atomic_fetch_max(&a.st->best[m], argmax_key(logit, row), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-__global__ __launch_bounds__(64) void k_cert_final(CertState* st, int M, int32_t* idx, float* maxv,
-                                                   int32_t* survivors) {
-  const int m = threadIdx.x;
-  const bool fallback = st->flag != 0u;
-  if (m < M) {
-    const unsigned long long key = st->best[m];
-    if (!fallback) {
-      idx[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
-      if (maxv) maxv[m] = key_value(key);
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint32_t d = __hip_atomic_fetch_add(&a.st->done[m], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == cm - 1u) {
+        const unsigned long long key = __hip_atomic_load(&a.st->best[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.idx[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+        if (a.maxv) a.maxv[m] = key_value(key);
+        if (a.survivors) a.survivors[m] = sat_i32(cm);
+        __hip_atomic_store(&a.st->best[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.st->done[m], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    if (survivors) {
-      const uint32_t c = st->count[m];
-      survivors[m] = c > 0x7FFFFFFFu ? 0x7FFFFFFF : (int32_t)c;
-    }
-  }
-  __syncthreads();  // every lane has read its row's state before any is cleared
-  if (m < kCertMaxM) {
-    st->best[m] = 0ull;
-    st->count[m] = 0u;
-    st->lower[m] = 0u;
   }
 }
 
@@ -368,9 +395,8 @@ hipError_t launch_cert(const w12_matrix* mat, const uint16_t* x, int64_t ldx, in
   a.cap = W12_CERT_MAX_SURVIVORS;
   const double ku = (double)mat->k * 0x1p-24;
   a.slack = 4.0 * ku / (1.0 - ku);
-  const dim3 grid(a.chunks, M);
-  hipLaunchKernelGGL(k_cert_lower, grid, dim3(kCertThreads), 0, s, a);
-  hipLaunchKernelGGL(k_cert_select, grid, dim3(kCertThreads), 0, s, a);
+  hipLaunchKernelGGL(k_cert_lower, dim3(a.chunks, M), dim3(kCertThreads), 0, s, a);
+  hipLaunchKernelGGL(k_cert_select, dim3(a.chunks, M), dim3(kCertThreads), 0, s, a);
   RescoreArgs r{};
   r.rec = mat->records;
   r.e_top = mat->e_top;
@@ -380,12 +406,14 @@ hipError_t launch_cert(const w12_matrix* mat, const uint16_t* x, int64_t ldx, in
   r.ldx = ldx;
   r.st = st;
   r.list = list;
+  r.idx = idx;
+  r.maxv = maxv;
+  r.survivors = survivors;
   r.n = a.n;
   r.k = a.k;
   r.m = M;
   r.cap = a.cap;
   hipLaunchKernelGGL(k_cert_rescore, dim3(kNumCU), dim3(kCertThreads), 0, s, r);
-  hipLaunchKernelGGL(k_cert_final, dim3(1), dim3(64), 0, s, st, M, idx, maxv, survivors);
   return hipGetLastError();
 }
 

@@ -246,15 +246,18 @@ hipError_t launch_rows_argmax(const float* y, int64_t ldy, int n, int M, unsigne
 
 // ------------------------------------------------------------------ certified LM head
 // Per-call state of the certified head (w12_certify.hip), in the workspace;
-// zero before a workspace's first use and cleared again by every call (the
-// fallback flag and the norms are rewritten each call).
+// zero before a workspace's first use. Every call leaves it ready for the
+// next: k_cert_lower restarts the survivor counts, k_cert_rescore clears the
+// lower bounds and rewrites the gate, and a row's last rescored pair clears
+// its key and done count.
 constexpr int kCertMaxM = 64;
 struct CertState {
   unsigned long long best[kCertMaxM];  // argmax keys of the rescored rows
   double xnorm[kCertMaxM];             // ||x_m||_2
   uint32_t lower[kCertMaxM];           // order-preserving key of the best lower bound
   uint32_t count[kCertMaxM];           // surviving rows
-  uint32_t flag;                       // nonzero: some activation row kept more than the cap
+  uint32_t done[kCertMaxM];            // survivors rescored
+  uint32_t flag;                       // any row over the cap: the full head's gate
 };
 int cert_chunks(int64_t n);
 hipError_t launch_cert_bounds(const w12_matrix* m, float* bounds, hipStream_t s);
