@@ -58,7 +58,8 @@
  *   (the K reduction is split over workgroups in a fixed order that depends
  *   only on N, K and M).
  * - Concurrent calls need distinct workspaces. The first W12_WS_COUNTER_BYTES
- *   of a GEMM workspace (W12_OP_GEMM, _GEMM_Q8, _LMHEAD_ARGMAX) are counter
+ *   of a GEMM workspace (W12_OP_GEMM, _GEMM_Q8, _LMHEAD_ARGMAX,
+ *   _LMHEAD_CERTIFIED) are counter
  *   words that must be zero before the workspace's first use (allocate it
  *   zero-filled once); every call leaves them zero again, so one workspace
  *   serves any sequence of GEMM calls, ops, matrices and sizes that fit in
@@ -83,7 +84,7 @@ extern "C" {
 #define W12_REC_BYTES 12288
 #define W12_REC_VIEW_BYTES 8192
 #define W12_MAX_M 64
-#define W12_WS_COUNTER_BYTES 16640 /* counter words at the start of a GEMM workspace */
+#define W12_WS_COUNTER_BYTES 50432 /* counter words at the start of a GEMM workspace */
 #define W12_NOALLOC_SCRATCH_BYTES (16u << 20) /* static scratch of w12_gemm_noalloc, per device */
 
 /* status codes */

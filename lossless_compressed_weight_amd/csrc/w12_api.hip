@@ -121,7 +121,8 @@ int choose_kernel(int64_t n, int64_t k, int64_t n_esc, int64_t M, int op, bool f
 size_t ws_bytes_any(int64_t n, int64_t k, int64_t M, int op);
 
 // Workspace of the certified head: [GEMM region shared by the Q pass and the
-// gated full head | CertState | Q logits [M][N] | chunk upper bounds | lists].
+// gated full head | CertCall | Q logits [M][N] | chunk upper bounds | lists]; CertZero sits in the
+// counter region at the start of the GEMM region.
 struct CertLayout {
   size_t gemm, state, logits, ub, list, total;
 };
@@ -130,7 +131,7 @@ CertLayout cert_layout(int64_t n, int64_t k, int64_t M) {
   const size_t g = std::max(ws_bytes_any(n, k, M, W12_OP_GEMM_Q8), ws_bytes_any(n, k, M, W12_OP_LMHEAD_ARGMAX));
   c.gemm = round256(g);
   c.state = c.gemm;
-  c.logits = c.state + round256(sizeof(CertState));
+  c.logits = c.state + round256(sizeof(CertCall));
   c.ub = c.logits + round256((size_t)M * (size_t)n * sizeof(float));
   c.list = c.ub + round256((size_t)M * (size_t)cert_chunks(n) * sizeof(float));
   c.total = c.list + round256((size_t)M * W12_CERT_MAX_SURVIVORS * sizeof(uint32_t));
@@ -160,18 +161,16 @@ DenseLayout dense_layout(int64_t n, int64_t k, int64_t M, int op) {
   return d;
 }
 
-// The two-pass argmax's workspace: [kernel plans of both ops | fp32 logits [M][N] | keys | counters], one
-// 256-byte line of keys and one of counters per activation row.
+// The two-pass argmax's workspace: [kernel plans of both ops | fp32 logits [M][N]]; its keys and
+// counters are in the counter region (kArgmaxStateOffset).
 struct ArgmaxLayout {
-  size_t main, logits, keys, ctr, total;
+  size_t main, logits, total;
 };
 ArgmaxLayout argmax_layout(int64_t n, int64_t k, int64_t M) {
   ArgmaxLayout L{};
   L.main = round256(std::max(ws_bytes_kernels(n, k, M, W12_OP_GEMM), ws_bytes_kernels(n, k, M, W12_OP_LMHEAD_ARGMAX)));
   L.logits = L.main;
-  L.keys = L.logits + round256((size_t)M * (size_t)n * sizeof(float));
-  L.ctr = L.keys + (size_t)W12_MAX_M * kArgmaxStateBytes;
-  L.total = L.ctr + (size_t)W12_MAX_M * kArgmaxStateBytes;
+  L.total = L.logits + round256((size_t)M * (size_t)n * sizeof(float));
   return L;
 }
 
@@ -261,8 +260,10 @@ int run_argmax_two_pass(const w12_matrix* m, const uint16_t* x, int64_t M, int64
                          gate, W12_KERNEL_MFMA_HELPER);
   if (r != W12_OK) return r;
   const hipError_t e = launch_rows_argmax(logits, m->n, (int)m->n, (int)M,
-                                          reinterpret_cast<unsigned long long*>(wsb + L.keys),
-                                          reinterpret_cast<uint32_t*>(wsb + L.ctr), idx, maxv, gate,
+                                          reinterpret_cast<unsigned long long*>(wsb + kArgmaxStateOffset),
+                                          reinterpret_cast<uint32_t*>(wsb + kArgmaxStateOffset +
+                                                                      W12_MAX_M * kArgmaxStateBytes),
+                                          idx, maxv, gate,
                                           reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "argmax of the stored logits: launch");
   return W12_OK;
@@ -571,19 +572,20 @@ int w12_lmhead_argmax_certified(const w12_matrix* m, const float* bounds, const 
   const CertLayout c = cert_layout(m->n, m->k, M);
   if (!ws || ws_bytes < c.total) return W12_E_WORKSPACE;
   char* wsb = reinterpret_cast<char*>(ws);
-  CertState* st = reinterpret_cast<CertState*>(wsb + c.state);
+  CertZero* z = reinterpret_cast<CertZero*>(wsb + kCertZeroOffset);
+  CertCall* cc = reinterpret_cast<CertCall*>(wsb + c.state);
   float* lq = reinterpret_cast<float*>(wsb + c.logits);
   // 1. Q-copy logits: the view with the escapes applied, fp32
   int r = run_gemm(m, x, M, ldx, lq, m->n, W12_F32, W12_OP_GEMM_Q8, true, ws, c.gemm, nullptr, nullptr, stream);
   if (r != W12_OK) return r;
   // 2. bounds, survivors, exact rescoring, indices
-  const hipError_t e = launch_cert(m, x, ldx, (int)M, lq, bounds, st, reinterpret_cast<float*>(wsb + c.ub),
+  const hipError_t e = launch_cert(m, x, ldx, (int)M, lq, bounds, z, cc, reinterpret_cast<float*>(wsb + c.ub),
                                    reinterpret_cast<uint32_t*>(wsb + c.list), idx, max_logit, survivors,
                                    reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "certified head kernels");
   // 3. the full fused head, which does nothing unless the fallback flag is up
   return run_gemm(m, x, M, ldx, nullptr, 0, W12_F32, W12_OP_LMHEAD_ARGMAX, true, ws, c.gemm, idx, max_logit, stream,
-                  &st->flag);
+                  &cc->flag);
 }
 
 int w12_validate(const w12_matrix* m, void* ws, size_t ws_bytes, void* stream) {

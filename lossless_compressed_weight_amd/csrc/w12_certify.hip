@@ -144,7 +144,8 @@ struct CertArgs {
   int64_t ldx;
   const float* lq;       // Q-copy logits [M][N], fp32
   const float* bounds;   // [N][2]: r_n, a_n
-  CertState* st;
+  CertZero* z;
+  CertCall* cc;
   float* ub_chunk;       // [M][chunks]
   uint32_t* list;        // [M][cap]
   int n, k, m, chunks, cap;
@@ -174,8 +175,8 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
   const int chunk = blockIdx.x, m = blockIdx.y;
   const double xn = row_norm(a.x + (int64_t)m * a.ldx, a.k, red);
   if (chunk == 0 && threadIdx.x == 0) {
-    a.st->xnorm[m] = xn;
-    a.st->count[m] = 0u;  // the survivors are counted by k_cert_select
+    a.cc->xnorm[m] = xn;
+    a.cc->count[m] = 0u;  // the survivors are counted by k_cert_select
   }
   float lo = -__builtin_inff(), hi = -__builtin_inff();
   const int r0 = chunk * kCertChunk;
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
       lo = fmaxf(lo, lo_w[w]);
       hi = fmaxf(hi, hi_w[w]);
     }
-    __hip_atomic_fetch_max(&a.st->lower[m], ord32(lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_max(&a.z->lower[m], ord32(lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     a.ub_chunk[(int64_t)m * a.chunks + chunk] = hi;
   }
 }
@@ -214,9 +215,9 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
 // surviving rows (the count may pass the cap; entries past it are dropped).
 __global__ __launch_bounds__(kCertThreads) void k_cert_select(CertArgs a) {
   const int chunk = blockIdx.x, m = blockIdx.y;
-  const float best_lower = unord32(a.st->lower[m]);
+  const float best_lower = unord32(a.z->lower[m]);
   if (a.ub_chunk[(int64_t)m * a.chunks + chunk] < best_lower) return;  // nothing here can win
-  const double xn = a.st->xnorm[m];
+  const double xn = a.cc->xnorm[m];
   const int lane = threadIdx.x & 63;
   const int r0 = chunk * kCertChunk;
   for (int base = 0; base < kCertChunk; base += kCertThreads) {
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_select(CertArgs a) {
     if (ballot == 0) continue;
     uint32_t pos0 = 0;
     if (lane == 0)
-      pos0 = __hip_atomic_fetch_add(&a.st->count[m], (uint32_t)__popcll(ballot), __ATOMIC_RELAXED,
+      pos0 = __hip_atomic_fetch_add(&a.cc->count[m], (uint32_t)__popcll(ballot), __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
     pos0 = __shfl(pos0, 0, 64);
     if (keep) {
@@ -248,7 +249,8 @@ struct RescoreArgs {
   const uint2* esc;
   const uint16_t* x;
   int64_t ldx;
-  CertState* st;
+  CertZero* z;
+  CertCall* cc;
   const uint32_t* list;
   int32_t* idx;
   float* maxv;
@@ -268,12 +270,12 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_rescore(RescoreArgs a) {
   const int lane = threadIdx.x & 63;
   // per-activation-row counts and their inclusive prefix (lane = row)
   uint32_t c = 0;
-  if (lane < a.m) c = a.st->count[lane];
+  if (lane < a.m) c = a.cc->count[lane];
   const bool fallback = __ballot(c > (uint32_t)a.cap) != 0ull;
   if (blockIdx.x == 0 && threadIdx.x < 64) {
     if (threadIdx.x == 0)
-      __hip_atomic_store(&a.st->flag, fallback ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane < kCertMaxM) a.st->lower[lane] = 0u;  // read by no kernel after k_cert_select
+      __hip_atomic_store(&a.cc->flag, fallback ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane < kCertMaxM) a.z->lower[lane] = 0u;  // read by no kernel after k_cert_select
     if (lane < a.m && (fallback || c == 0u)) {
       // the full head answers (or, with no survivor at all, which the bounds
       // rule out, index 0): only the counts are reported here
@@ -350,16 +352,16 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_rescore(RescoreArgs a) {
     if (lane == 0) {
       // the key and the count are atomics at the coherence point; the count
       // goes in only once the key has, so the row's last pair reads them all
-      __hip_atomic_fetch_max(&a.st->best[m], argmax_key(logit, row), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_max(&a.z->best[m], argmax_key(logit, row), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_s_waitcnt(0);
-      const uint32_t d = __hip_atomic_fetch_add(&a.st->done[m], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t d = __hip_atomic_fetch_add(&a.z->done[m], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (d == cm - 1u) {
-        const unsigned long long key = __hip_atomic_load(&a.st->best[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long key = __hip_atomic_load(&a.z->best[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         a.idx[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
         if (a.maxv) a.maxv[m] = key_value(key);
         if (a.survivors) a.survivors[m] = sat_i32(cm);
-        __hip_atomic_store(&a.st->best[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.st->done[m], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.z->best[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.z->done[m], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -378,14 +380,15 @@ hipError_t launch_cert_bounds(const w12_matrix* m, float* bounds, hipStream_t s)
 int cert_chunks(int64_t n) { return (int)((n + kCertChunk - 1) / kCertChunk); }
 
 hipError_t launch_cert(const w12_matrix* mat, const uint16_t* x, int64_t ldx, int M, const float* lq,
-                       const float* bounds, CertState* st, float* ub_chunk, uint32_t* list, int32_t* idx,
+                       const float* bounds, CertZero* z, CertCall* cc, float* ub_chunk, uint32_t* list, int32_t* idx,
                        float* maxv, int32_t* survivors, hipStream_t s) {
   CertArgs a{};
   a.x = x;
   a.ldx = ldx;
   a.lq = lq;
   a.bounds = bounds;
-  a.st = st;
+  a.z = z;
+  a.cc = cc;
   a.ub_chunk = ub_chunk;
   a.list = list;
   a.n = (int)mat->n;
@@ -404,7 +407,8 @@ hipError_t launch_cert(const w12_matrix* mat, const uint16_t* x, int64_t ldx, in
   r.esc = reinterpret_cast<const uint2*>(mat->esc);
   r.x = x;
   r.ldx = ldx;
-  r.st = st;
+  r.z = z;
+  r.cc = cc;
   r.list = list;
   r.idx = idx;
   r.maxv = maxv;

@@ -29,7 +29,15 @@ constexpr size_t kCounterBytes = W12_WS_COUNTER_BYTES;
 // Escape lines per matrix row (escapes x padded activation rows / N) above
 // which the MFMA kernel reads escape activations from a transposed copy of x.
 constexpr int64_t kXtEscRowLines = 16;
-static_assert(kCounterBytes >= (kMaxGrid + 1) * sizeof(uint32_t), "counter region too small");
+// Layout of the counter region: the GEMM kernels' counters, then the state of
+// the two-pass argmax (a line of keys and a line of counters per activation
+// row), then the certified head's accumulators. All of it is zero between
+// calls, at the same place for every op and M, so one workspace serves any mix.
+constexpr size_t kKernelCounterBytes = 16640;
+constexpr size_t kArgmaxStateOffset = kKernelCounterBytes;
+constexpr size_t kArgmaxStateBytes = 256;  // per activation row, keys and counters each
+constexpr size_t kCertZeroOffset = kArgmaxStateOffset + 2 * W12_MAX_M * kArgmaxStateBytes;
+static_assert(kKernelCounterBytes >= (kMaxGrid + 1) * sizeof(uint32_t), "counter region too small");
 
 typedef short short2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -239,30 +247,32 @@ hipError_t launch_fix_dense(const FixParams& p, hipStream_t s);
 // then this kernel folds each row (w12_argmax.hip). keys and ctr hold one
 // 256-byte line per activation row (kArgmaxStateBytes), zero before the call;
 // the last workgroup of each row clears its line again.
-constexpr size_t kArgmaxStateBytes = 256;
 constexpr int kFusedArgmaxMaxM = 16;  // the fused argmax keeps its per-lane fold up to here
 hipError_t launch_rows_argmax(const float* y, int64_t ldy, int n, int M, unsigned long long* keys, uint32_t* ctr,
                               int32_t* idx, float* maxv, const uint32_t* gate, hipStream_t s);
 
 // ------------------------------------------------------------------ certified LM head
-// Per-call state of the certified head (w12_certify.hip), in the workspace;
-// zero before a workspace's first use. Every call leaves it ready for the
-// next: k_cert_lower restarts the survivor counts, k_cert_rescore clears the
-// lower bounds and rewrites the gate, and a row's last rescored pair clears
-// its key and done count.
+// State of the certified head (w12_certify.hip). CertZero accumulates, so it
+// lives in the counter region (kCertZeroOffset): zero before a workspace's
+// first use and left zero by every call (k_cert_rescore clears the lower
+// bounds, a row's last rescored pair its key and done count). CertCall is
+// written by every call before it is read.
 constexpr int kCertMaxM = 64;
-struct CertState {
+struct CertZero {
   unsigned long long best[kCertMaxM];  // argmax keys of the rescored rows
-  double xnorm[kCertMaxM];             // ||x_m||_2
   uint32_t lower[kCertMaxM];           // order-preserving key of the best lower bound
-  uint32_t count[kCertMaxM];           // surviving rows
   uint32_t done[kCertMaxM];            // survivors rescored
+};
+struct CertCall {
+  double xnorm[kCertMaxM];             // ||x_m||_2
+  uint32_t count[kCertMaxM];           // surviving rows
   uint32_t flag;                       // any row over the cap: the full head's gate
 };
+static_assert(kCertZeroOffset + sizeof(CertZero) <= kCounterBytes, "counter region too small");
 int cert_chunks(int64_t n);
 hipError_t launch_cert_bounds(const w12_matrix* m, float* bounds, hipStream_t s);
 hipError_t launch_cert(const w12_matrix* mat, const uint16_t* x, int64_t ldx, int M, const float* lq,
-                       const float* bounds, CertState* st, float* ub_chunk, uint32_t* list, int32_t* idx,
+                       const float* bounds, CertZero* z, CertCall* cc, float* ub_chunk, uint32_t* list, int32_t* idx,
                        float* maxv, int32_t* survivors, hipStream_t s);
 
 // ------------------------------------------------------------------ stream kernel

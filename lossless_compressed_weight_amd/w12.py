@@ -26,7 +26,7 @@ FORMAT_VERSION = 1
 REC_ROWS, REC_COLS, REC_BYTES, REC_VIEW_BYTES = 16, 512, 12288, 8192
 MAX_M = 64
 NOALLOC_SCRATCH_BYTES = 16 << 20
-WS_COUNTER_BYTES = 16640
+WS_COUNTER_BYTES = 50432
 OK, E_INVALID_ARG, E_UNSUPPORTED_SHAPE, E_M_RANGE, E_WORKSPACE, E_VERSION, E_HIP, E_NOT_IMPLEMENTED, E_CORRUPT = (
     0, -1, -2, -3, -4, -5, -6, -7, -8)
 BF16, F32 = 0, 1

@@ -195,3 +195,22 @@ def test_certified_lm_head_151936_full(lm_head, m):
     mat, bounds, r, a, data = lm_head
     x, y, yq = data[m]
     _check_call(mat, bounds, x, y, yq, r, a, f"lm head M={m}")
+
+
+def test_certified_workspace_reused_across_sizes():
+    """One workspace, sized for the largest call, serves calls of different M
+    in any order: the state that accumulates sits at a fixed place and every
+    call leaves it clear."""
+    w = synth.workload_matrix(3, 0, rows=slice(0, 4096))
+    mat = w12.encode(dev16(w))
+    bounds = w12.certify_bounds(mat)
+    ws = w12.new_workspace(w12.OP_LMHEAD_CERTIFIED, 4096, 5120, 64)
+    for m in (33, 3, 64, 1, 17, 64):
+        x = synth.make_activations(m, 5120, seed=1300 + m)
+        idx = torch.empty(m, dtype=torch.int32, device="cuda")
+        mx = torch.empty(m, dtype=torch.float32, device="cuda")
+        w12.w12_lmhead_argmax_certified(mat, bounds, dev16(x), idx, mx, None, ws)
+        ridx, margin = o.argmax_ref(o.gemm_ref(x, w))
+        far = margin >= 1e-3
+        assert np.array_equal(idx.cpu().numpy()[far], ridx[far]), f"M={m}"
+    assert int(ws[: w12.WS_COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
