@@ -114,7 +114,7 @@ int choose_kernel(int64_t n, int64_t k, int64_t n_esc, int64_t M, int op, bool f
   if (g_tune_path == 3) return mx_ok ? W12_KERNEL_MFMA_STREAM : W12_KERNEL_MFMA_HELPER;
   if (!old.mfma) return W12_KERNEL_GEMV;
   const bool few_tiles = (n / 16 + 3) / 4 < kNumCU;
-  if (mx_ok && M <= 32 && few_tiles && (!fix || n_esc <= kMxMaxEscPerRow * n)) return W12_KERNEL_MFMA_STREAM;
+  if (mx_ok && few_tiles && (!fix || n_esc <= kMxMaxEscPerRow * n)) return W12_KERNEL_MFMA_STREAM;
   return W12_KERNEL_MFMA_HELPER;
 }
 

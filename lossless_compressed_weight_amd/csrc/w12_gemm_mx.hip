@@ -27,10 +27,13 @@
 // segment's stream: the partial sums get x * (-placeholder) then x * exact,
 // two fused multiply-adds per activation row (exact when x is one-hot).
 //
-// Activations. The B operand of v_mfma_f32_16x16x32_bf16 is read straight
-// from row-major x: lane l takes activation row l % 16 of its m-tile and 16
-// consecutive columns, two 16-byte loads, matching the 16 columns of the
-// view load that give its A operands.
+// Activations. The B operand of v_mfma_f32_16x16x32_bf16 comes from
+// row-major x with no pre-pass: lane l needs activation row l % 16 of its
+// m-tile at the 16 columns of the view load that give its A operands. Read
+// that way, one load instruction would touch 16 rows' lines, half of each;
+// instead each wave loads its 64-column chunk as whole 128-byte lines (eight
+// rows per instruction) and turns it into operand order through a small
+// per-wave LDS area.
 //
 // End of a segment. Each wave leaves its MFMA accumulators in LDS; after a
 // barrier all 512 threads add the eight waves' sums in wave order and either
@@ -51,6 +54,7 @@ constexpr int kUnitCols = 64 * kWaves;     // a unit: one 64-column chunk per wa
 constexpr int kWgPerCU = 8 / kWaves;       // workgroups per compute unit (eight waves per CU)
 constexpr int kCap = 256;  // escape substitutions one wave holds per segment
 constexpr int kRedRow = 65;  // floats per row of the reduction area (64 lanes + 1 of padding)
+constexpr int kXsRow = 144;  // bytes per activation row of a wave's staging area (128 + 16 of padding)
 
 template <int MT>
 constexpr int kRG = MT <= 2 ? 4 : 2;  // 16-row blocks of a whole tile
@@ -153,6 +157,9 @@ struct Lds {
   uint2 list[kWaves][kCap];
   uint32_t rp[kWaves][65];
   int last[2];  // split tiles this workgroup finishes last: tile + 1, or 0
+  // per wave: its 64-column chunk of x for the current unit, rows padded to
+  // 144 bytes so that the operand-order reads spread over the banks
+  alignas(16) uint8_t xs[kWaves][16 * MT][kXsRow];
 };
 
 // -------------------------------------------------------------- decode
@@ -331,18 +338,23 @@ __device__ __forceinline__ int seg_stream(const MxParams& a, Lds<MT>& sh, const 
   const uint8_t* blk = a.rec + (int64_t)(s.row0 >> 4) * a.kb * kRecBytes;
   const uint32_t blk_stride = (uint32_t)a.kb * kRecBytes;
   const uint32_t voff = (uint32_t)lane * 16u, boff = kViewBytes + (uint32_t)lane * 8u;
-  const uint16_t* xr[MT];
+  // Activations: load i of a unit takes rows 8 i .. 8 i + 7 of the wave's
+  // 64-column chunk, lane l row 8 i + l / 8 and bytes 16 (l % 8) of its
+  // 128, so each load is eight whole lines (rows past M read row M - 1;
+  // they only feed outputs that are not stored).
+  const uint16_t* xr[2 * MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = min(mt * 16 + (lane & 15), a.m - 1);
-    xr[mt] = a.x + (int64_t)m * a.ldx + wave * 64 + (lane >> 4) * 16;
-  }
+  for (int i = 0; i < 2 * MT; ++i)
+    xr[i] = a.x + (int64_t)min(8 * i + (lane >> 3), a.m - 1) * a.ldx + wave * 64 + (lane & 7) * 8;
+  uint8_t* xs = &sh.xs[wave][0][0];
+  const uint32_t xs_w = (uint32_t)(lane >> 3) * kXsRow + (uint32_t)(lane & 7) * 16u;
+  const uint32_t xs_r = (uint32_t)(lane & 15) * kXsRow + (uint32_t)(lane >> 4) * 32u;
   auto load = [&](Stage<MT, RG, Q>& st, int u) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      st.x[mt][0] = *reinterpret_cast<const uint4*>(xr[mt] + (int64_t)u * kUnitCols);
-      st.x[mt][1] = *reinterpret_cast<const uint4*>(xr[mt] + (int64_t)u * kUnitCols + 8);
-    }
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        st.x[mt][h] = *reinterpret_cast<const uint4*>(xr[2 * mt + h] + (int64_t)u * kUnitCols);
     // this wave's 64-column chunk c of the row: record c / 8, chunk c % 8 in it
     const uint32_t c = (uint32_t)u * kWaves + (uint32_t)wave;
     const uint32_t rec_off = (c >> 3) * kRecBytes;
@@ -360,6 +372,23 @@ __device__ __forceinline__ int seg_stream(const MxParams& a, Lds<MT>& sh, const 
     for (int mt = 0; mt < MT; ++mt) acc[j][mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   int ne = 0;  // escape substitutions in the list
   auto compute = [&](const Stage<MT, RG, Q>& st, int u) {
+    // through LDS into operand order: lane l gets activation row l % 16 of
+    // each m-tile, bytes 32 (l / 16) .. +31 of the chunk (the columns of its
+    // A operands). One wave's LDS accesses complete in order, so the next
+    // unit's writes cannot overtake these reads.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4_t*>(xs + xs_w + (2 * mt + h) * 8 * kXsRow) = __builtin_bit_cast(u32x4_t, st.x[mt][h]);
+    __builtin_amdgcn_wave_barrier();
+    uint4 xb[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      xb[mt][0] = __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4_t*>(xs + xs_r + mt * 16 * kXsRow));
+      xb[mt][1] = __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4_t*>(xs + xs_r + mt * 16 * kXsRow + 16));
+    }
+    __builtin_amdgcn_wave_barrier();
     uint32_t d[RG][8];
 #pragma unroll
     for (int j = 0; j < RG; ++j) decode16<Q>(st.v[j], Q ? make_uint2(0, 0) : st.b[j], d[j], bias[j]);
@@ -379,10 +408,10 @@ __device__ __forceinline__ int seg_stream(const MxParams& a, Lds<MT>& sh, const 
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0),
-                                                             __builtin_bit_cast(bf16x8_t, st.x[mt][0]), acc[j][mt], 0,
+                                                             __builtin_bit_cast(bf16x8_t, xb[mt][0]), acc[j][mt], 0,
                                                              0, 0);
         acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1),
-                                                             __builtin_bit_cast(bf16x8_t, st.x[mt][1]), acc[j][mt], 0,
+                                                             __builtin_bit_cast(bf16x8_t, xb[mt][1]), acc[j][mt], 0,
                                                              0, 0);
       }
     }

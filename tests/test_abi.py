@@ -166,7 +166,7 @@ def test_plan_arithmetic(n, k, m):
                 assert plan["kernel"] in (w12.KERNEL_GEMV, w12.KERNEL_MFMA_HELPER)
             if m <= 2:
                 assert plan["kernel"] == w12.KERNEL_GEMV
-            elif -(-(n // 16) // 4) < 256 and m <= 32 and op != w12.OP_LMHEAD_ARGMAX:
+            elif -(-(n // 16) // 4) < 256 and op != w12.OP_LMHEAD_ARGMAX:
                 assert plan["kernel"] == w12.KERNEL_MFMA_STREAM and plan["prepass"] == int(dense)
             else:
                 assert plan["kernel"] == w12.KERNEL_MFMA_HELPER
