@@ -243,13 +243,17 @@ int w12_validate(const w12_matrix* m, void* ws, size_t ws_bytes, void* stream);
  *   default; any M <= 16 when forced).
  * MFMA_HELPER: v_mfma_f32_16x16x32_bf16 with four streaming waves and a
  *   helper wave that applies the escape corrections; an activation transpose
- *   kernel runs first. The default from M = 3 for N > 16320, and always for the LM-head
+ *   kernel runs first beyond 16 activation rows, and up to 16 only for
+ *   matrices with many escapes per workgroup (w12_plan.prepass). The default
+ *   from M = 3 where the stream kernel is not, and always for the LM-head
  *   argmax (fused up to 16 activation rows; above, it stores fp32 logits and
  *   a row-argmax kernel follows) and for K > 2^20.
  * MFMA_STREAM: v_mfma_f32_16x16x32_bf16 with eight streaming waves, escapes
  *   substituted into the decoded weights in registers, activations read
  *   from x through LDS; no pre-pass. The default from M = 3 when the matrix
- *   has fewer 64-row tiles than the GPU has compute units (N <= 16320).
+ *   has fewer 64-row tiles than the GPU has compute units (N <= 16320),
+ *   except up to 16 activation rows on matrices with K > 8192 or fewer than
+ *   32 tiles (N <= 1984).
  * With more than 8 escapes per row on average, the exact GEMM and the Q pass
  * with escapes run the chosen kernel without escape work into fp32 sums and
  * a fix-up kernel applies the escapes (w12_plan.fixup). */

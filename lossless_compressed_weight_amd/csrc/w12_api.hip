@@ -106,6 +106,29 @@ bool dense_path(const w12_matrix* m, int op, bool fix) {
 // argmax, dense escapes and very long rows. Measured per call on MI355X at
 // M = 32: 6144 x 5120 21.0 vs 23.9 us, 5120 x 6144 20.6 vs 24.0,
 // 5120 x 17408 37.4 vs 37.5, 17408 x 5120 37.3 vs 32.2 (stream vs helper).
+// The copies of x that one activation transpose kernel writes before the
+// helper-wave MFMA kernel: beyond 16 activation rows its B operands in operand
+// order (xk; up to 16 rows the kernel stages x through LDS itself), and, with
+// many escapes per row, the activations of each escape column (xT: one cache
+// line per escape instead of one per activation row). Up to 16 rows the
+// escapes' activations are gathered from x unless a workgroup has more than
+// kGatherEscPerWg of them (measured at M = 16: the 151936-row LM head, ~830
+// per workgroup, 6% slower gathering; 17408x5120, ~93, 2% faster with no
+// pre-pass at all, 8% at M = 3..8).
+constexpr int64_t kGatherEscPerWg = 256;
+struct XCopies {
+  bool xt, xk;
+};
+XCopies x_copies(const w12_matrix* m, const GemmPlan& pl, int64_t M, bool fix) {
+  XCopies c{false, false};
+  if (!pl.mfma) return c;
+  const int64_t mm = ((M + 15) / 16) * 16;
+  c.xk = M > 16;
+  const bool many = fix && m->n_esc > 0 && m->n_esc * mm > kXtEscRowLines * m->n;
+  c.xt = many && (c.xk || m->n_esc > kGatherEscPerWg * (int64_t)pl.P);
+  return c;
+}
+
 int choose_kernel(int64_t n, int64_t k, int64_t n_esc, int64_t M, int op, bool fix, const GemmPlan& old) {
   const bool mx_ok = op != W12_OP_LMHEAD_ARGMAX && k <= kMxMaxK;
   if (g_tune_path == 4) fix = false;  // the dense path runs its GEMM without escape work
@@ -113,8 +136,13 @@ int choose_kernel(int64_t n, int64_t k, int64_t n_esc, int64_t M, int op, bool f
   if (g_tune_path == 2) return W12_KERNEL_MFMA_HELPER;
   if (g_tune_path == 3) return mx_ok ? W12_KERNEL_MFMA_STREAM : W12_KERNEL_MFMA_HELPER;
   if (!old.mfma) return W12_KERNEL_GEMV;
-  const bool few_tiles = (n / 16 + 3) / 4 < kNumCU;
-  if (mx_ok && few_tiles && (!fix || n_esc <= kMxMaxEscPerRow * n)) return W12_KERNEL_MFMA_STREAM;
+  const int64_t tiles = (n / 16 + 3) / 4;  // 64-row tiles
+  // Up to 16 activation rows the helper-wave kernel runs without a pre-pass
+  // and is the faster one on long rows and on matrices of few tiles
+  // (measured at M = 8: 5120x17408 29.1 against 31.4 us, 1024x5120 12.8
+  // against 14.3; 6144x5120, 5120x6144 and 8192x5120 within 1 us either way).
+  const bool stream_rows = M > 16 || (tiles >= 32 && k <= 8192);
+  if (mx_ok && tiles < kNumCU && stream_rows && (!fix || n_esc <= kMxMaxEscPerRow * n)) return W12_KERNEL_MFMA_STREAM;
   return W12_KERNEL_MFMA_HELPER;
 }
 
@@ -313,19 +341,15 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   p.q = op == W12_OP_GEMM_Q8;
   p.gate = gate;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // The helper-wave MFMA kernel's escape fix-up needs the activations of each
-  // escape column for all rows. With many escapes per row it reads them from
-  // a transposed copy of x (one cache line per escape instead of one per
-  // activation row), with few it gathers them from x directly. It also reads
-  // its B operands from a copy of x in operand order (fully coalesced loads);
-  // one kernel writes both copies before it.
+  // the copies of x the helper-wave kernel reads (x_copies)
   p.xt = nullptr;
   p.xk = nullptr;
-  if (pl.mfma) {
+  const XCopies xc = x_copies(m, pl, M, p.fix != 0);
+  if (xc.xt || xc.xk) {
     const int64_t mm = ((M + 15) / 16) * 16;
     char* xt_at = wsb + round256(pl.ctr_bytes) + round256(pl.part_bytes) + round256(pl.key_bytes);
-    uint16_t* xt = (p.fix && m->n_esc * mm > kXtEscRowLines * m->n) ? reinterpret_cast<uint16_t*>(xt_at) : nullptr;
-    uint16_t* xk = reinterpret_cast<uint16_t*>(xt_at + round256(pl.xt_bytes));
+    uint16_t* xt = xc.xt ? reinterpret_cast<uint16_t*>(xt_at) : nullptr;
+    uint16_t* xk = xc.xk ? reinterpret_cast<uint16_t*>(xt_at + round256(pl.xt_bytes)) : nullptr;
     const hipError_t ex = launch_xpose(x, ldx, (int)M, (int)mm, (int)m->k, xt, xk, gate, st);
     if (ex != hipSuccess) return hip_fail(ex, "activation transpose launch");
     p.xt = xt;
@@ -457,7 +481,8 @@ int w12_plan_info(const w12_matrix* m, int op, int64_t M, uint32_t flags, w12_pl
     o.split_tile_rows = pl.tile_rows;
     o.unit_cols = 256;
     o.split_units = pl.sk_units;
-    o.prepass = pl.mfma ? 1 : 0;
+    const XCopies xc = x_copies(m, pl, M, fix);
+    o.prepass = xc.xt || xc.xk ? 1 : 0;
     o.workspace_bytes = gemm_ws_bytes(pl);
   }
   if (dense) {

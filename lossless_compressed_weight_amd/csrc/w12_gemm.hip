@@ -1249,32 +1249,59 @@ struct MfmaStage {
 template <int MT>
 struct MfmaLds {
   alignas(16) float part[2][kStreamWaves][kMfmaR<MT>][MT][4][64];  // C of each tile and m-tile, double-buffered
+  // up to 16 activation rows: each streaming wave's 64-column chunk of x on
+  // its way into operand order, 16-byte slots swizzled by row (see mfma_group)
+  alignas(16) uint8_t xs[MT == 1 ? kStreamWaves : 1][MT == 1 ? 16 : 1][MT == 1 ? 128 : 16];
   HelperLds<MT * 16, kMfmaR<MT> * 16> h;
 };
 
 // One segment: the RG 16-row blocks starting at block s, units [k0, k1).
 template <int MT, int RG, bool Q>
 __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, int k1, int wave, int lane,
-                                           float (*part)[kMfmaR<MT>][MT][4][64], int seg, const uint32_t* consumed) {
+                                           float (*part)[kMfmaR<MT>][MT][4][64], int seg, const uint32_t* consumed,
+                                           uint8_t* xs) {
   f32x4_t acc[RG][MT];
 #pragma unroll
   for (int j = 0; j < RG; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[j][mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const uint32_t c3800 = opaque_vgpr(0x38003800u);
-  // B operands from the copy of x in operand order: for chunk c, MFMA half h
-  // and m-tile mt, lane l's 8 activations (row mt*16 + l%16, columns
-  // 16 (l/16) + 8h + 0..7 of the chunk) are bytes 16 l of one contiguous
-  // kilobyte, so each load is fully coalesced.
+  // B operands: for chunk c, MFMA half h and m-tile mt, lane l needs the 8
+  // activations of row mt*16 + l%16 at columns 16 (l/16) + 8h + 0..7 of the
+  // chunk. From 17 rows on they come from the copy of x in operand order (one
+  // contiguous kilobyte per load). Up to 16 rows the wave loads its chunk of
+  // row-major x as whole 128-byte lines instead, rows 8h .. 8h + 7 in load h
+  // (lane l: row 8h + l/8, bytes 16 (l%8); rows past M read row M - 1, which
+  // only feeds outputs that are not stored), and turns it into operand order
+  // through its LDS area, where 16-byte slot j of row r sits at slot
+  // j ^ ((r / 2) % 8) so that the rows an operand read takes hit different
+  // banks. (Beyond one m-tile the kernel's LDS has no room for this, and the
+  // round trip in every unit cost more than the copy.)
   const uint8_t* xk = reinterpret_cast<const uint8_t*>(a.xk) + lane * 16;
+  uint32_t xo[2] = {0u, 0u}, xs_w[2] = {0u, 0u}, xs_r[2] = {0u, 0u};
+  if constexpr (MT == 1) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t rw = 8u * h + (uint32_t)(lane >> 3), rr = (uint32_t)(lane & 15);
+      xo[h] = 2u * ((uint32_t)min((int)rw, a.m - 1) * (uint32_t)a.ldx + (uint32_t)(wave * 64 + (lane & 7) * 8));
+      xs_w[h] = rw * 128u + ((((uint32_t)lane & 7u) ^ ((rw >> 1) & 7u)) << 4);
+      xs_r[h] = rr * 128u + ((((uint32_t)(lane >> 4) * 2u + h) ^ ((rr >> 1) & 7u)) << 4);
+    }
+  }
+  const char* xrow = reinterpret_cast<const char*>(a.x);
   const uint8_t* blk = a.rec + (int64_t)s * a.kb * kRecBytes;
   const uint32_t blk_stride = (uint32_t)(a.kb * kRecBytes);
   auto load = [&](MfmaStage<MT, RG, Q>& st, int kk) {
     const int c = kk * 4 + wave;
+    if constexpr (MT == 1) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      st.x[mt][0] = *reinterpret_cast<const uint4*>(xk + ((size_t)(2 * c) * MT + mt) * 1024);
-      st.x[mt][1] = *reinterpret_cast<const uint4*>(xk + ((size_t)(2 * c + 1) * MT + mt) * 1024);
+      for (int h = 0; h < 2; ++h) st.x[0][h] = *reinterpret_cast<const uint4*>(xrow + (xo[h] + (uint32_t)kk * 512u));
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        st.x[mt][0] = *reinterpret_cast<const uint4*>(xk + ((size_t)(2 * c) * MT + mt) * 1024);
+        st.x[mt][1] = *reinterpret_cast<const uint4*>(xk + ((size_t)(2 * c + 1) * MT + mt) * 1024);
+      }
     }
     const uint32_t rec_off = (uint32_t)(c >> 3) * kRecBytes;
 #pragma unroll
@@ -1285,6 +1312,20 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
     }
   };
   auto compute = [&](const MfmaStage<MT, RG, Q>& st) {
+    uint4 xb[MT][2];
+    if constexpr (MT == 1) {
+      // one wave's LDS accesses complete in order, so the next unit's writes
+      // cannot overtake these reads
+#pragma unroll
+      for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4_t*>(xs + xs_w[h]) = __builtin_bit_cast(u32x4_t, st.x[0][h]);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int h = 0; h < 2; ++h) xb[0][h] = __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4_t*>(xs + xs_r[h]));
+      __builtin_amdgcn_wave_barrier();
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xb[mt][0] = st.x[mt][0], xb[mt][1] = st.x[mt][1];
+    }
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
       uint32_t d[8];
@@ -1294,10 +1335,10 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0),
-                                                             __builtin_bit_cast(bf16x8_t, st.x[mt][0]),
+                                                             __builtin_bit_cast(bf16x8_t, xb[mt][0]),
                                                              acc[j][mt], 0, 0, 0);
         acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1),
-                                                             __builtin_bit_cast(bf16x8_t, st.x[mt][1]),
+                                                             __builtin_bit_cast(bf16x8_t, xb[mt][1]),
                                                              acc[j][mt], 0, 0, 0);
       }
     }
@@ -1360,14 +1401,14 @@ __global__ __launch_bounds__(kThreads) void k_mfma(GemmParams a) {
     const int b = s.row0 >> 4;  // first 16-row block
     if constexpr (R == 4) {
       switch (s.rg) {
-        case 1: mfma_group<MT, 1, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
-        case 2: mfma_group<MT, 2, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
-        case 3: mfma_group<MT, 3, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
-        default: mfma_group<MT, 4, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed); break;
+        case 1: mfma_group<MT, 1, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed, &sh.xs[MT == 1 ? wave : 0][0][0]); break;
+        case 2: mfma_group<MT, 2, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed, &sh.xs[MT == 1 ? wave : 0][0][0]); break;
+        case 3: mfma_group<MT, 3, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed, &sh.xs[MT == 1 ? wave : 0][0][0]); break;
+        default: mfma_group<MT, 4, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed, &sh.xs[MT == 1 ? wave : 0][0][0]); break;
       }
     } else {
-      if (s.rg == 1) mfma_group<MT, 1, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed);
-      else mfma_group<MT, 2, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed);
+      if (s.rg == 1) mfma_group<MT, 1, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed, &sh.xs[MT == 1 ? wave : 0][0][0]);
+      else mfma_group<MT, 2, Q>(a, b, s.k0, s.k1, wave, lane, sh.part[i & 1], i, &sh.h.consumed, &sh.xs[MT == 1 ? wave : 0][0][0]);
     }
     if (lane == 0) lds_add(&sh.h.ready[i & 1]);
   }

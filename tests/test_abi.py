@@ -166,7 +166,7 @@ def test_plan_arithmetic(n, k, m):
                 assert plan["kernel"] in (w12.KERNEL_GEMV, w12.KERNEL_MFMA_HELPER)
             if m <= 2:
                 assert plan["kernel"] == w12.KERNEL_GEMV
-            elif -(-(n // 16) // 4) < 256 and op != w12.OP_LMHEAD_ARGMAX:
+            elif (tiles := -(-(n // 16) // 4)) < 256 and op != w12.OP_LMHEAD_ARGMAX and (m > 16 or (tiles >= 32 and k <= 8192)):
                 assert plan["kernel"] == w12.KERNEL_MFMA_STREAM and plan["prepass"] == int(dense)
             else:
                 assert plan["kernel"] == w12.KERNEL_MFMA_HELPER
