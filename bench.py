@@ -533,6 +533,24 @@ def main():
                      "timing": "per-call time = back-to-back calls between one HIP event pair on the launch stream",
                      "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"})
 
+    # M scan (SpecPilot Appendix E: W12 time flat in the activation rows): gate and down of config 1
+    # at every M the library takes, each with the kernel the library chooses
+    m_scan = None
+    if not args.no_workloads:
+        m_scan = []
+        for i in (0, 2):
+            c = encoded[i]
+            n, k = c[0].n, c[0].k
+            for m in (1, 2, 3, 4, 8, 16, 24, 32, 48, 64):
+                x = torch.from_numpy(synth.make_activations(m, k, seed=synth.activation_seed(1, i, m)).view(np.int16)).to(dev)
+                y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                ws = w12.new_workspace(w12.OP_GEMM, n, k, m, dev)
+                us = time_shape(torch, w12, stream, c, x, y, ws, max(args.steps, 10))
+                plan = w12.plan_info(c[0], w12.OP_GEMM, m)
+                m_scan.append({"matrix": names[i], "m": m, "us": round(us, 2),
+                               "packed_gbs": round(n * k * 3 // 2 / us / 1e3, 1), "kernel": plan["kernel_name"],
+                               "prepass": plan["prepass"]})
+
     extra = None
     if not args.no_workloads:
         del encoded
@@ -551,7 +569,7 @@ def main():
                       "global_batch": list(ms), "seq_len": 1, "parallelism": "none"},
            "pct_peak": round(100 * value / PEAK_GBS, 2),
            "per_call": per_call, "roofline": roofline, "roofline_by_kernel": rl_all, "probe": probe,
-           "workloads": extra, "cpu_baseline": cpu, "gemm_sources_sha256": gemm_sources_sha256()}
+           "m_scan": m_scan, "workloads": extra, "cpu_baseline": cpu, "gemm_sources_sha256": gemm_sources_sha256()}
     print(json.dumps(out), flush=True)
 
 
