@@ -172,6 +172,24 @@ def test_plan_arithmetic(n, k, m):
                 assert plan["kernel"] == w12.KERNEL_MFMA_HELPER
 
 
+@pytest.mark.parametrize("m", [3, 8, 16, 17, 32])
+def test_helper_prepass_rule(m):
+    """Whether the helper-wave MFMA kernel's activation pre-pass runs: always
+    beyond 16 activation rows (the operand-order copy); up to 16 rows only
+    for the transposed copy, when escapes are many per row (escape lines
+    above 16 per row) and more than 256 per workgroup."""
+    n, k = 17408, 5120   # 272 tiles: the helper-wave kernel at every M from 3
+    for op, flags in ((w12.OP_GEMM, 0), (w12.OP_GEMM_Q8, 0), (w12.OP_GEMM_Q8, w12.Q8_APPLY_ESCAPES),
+                      (w12.OP_LMHEAD_ARGMAX, 0)):
+        fix = op != w12.OP_GEMM_Q8 or flags != 0
+        for n_esc in (0, 2000, 24000, 100000):
+            plan = w12.plan_info(_mat(n, k, n_esc=n_esc), op, m, flags)
+            assert plan["kernel"] == w12.KERNEL_MFMA_HELPER, plan
+            many_lines = fix and n_esc * 16 * -(-m // 16) > 16 * n
+            want = m > 16 or (many_lines and n_esc > 256 * plan["grid"])
+            assert plan["prepass"] == int(want), (op, flags, n_esc, m, plan)
+
+
 @pytest.mark.parametrize("path,n,k", [
     (2, 12784, 5120),   # helper-wave kernel: 799 row blocks in 200 tiles on 200 workgroups
     (3, 16368, 1024),   # stream kernel: 1023 row blocks in 256 tiles on 256 workgroups
