@@ -149,8 +149,8 @@ int choose_kernel(int64_t n, int64_t k, int64_t n_esc, int64_t M, int op, bool f
 size_t ws_bytes_any(int64_t n, int64_t k, int64_t M, int op);
 
 // Workspace of the certified head: [GEMM region shared by the Q pass and the
-// gated full head | CertCall | Q logits [M][N] | chunk upper bounds | lists]; CertZero sits in the
-// counter region at the start of the GEMM region.
+// gated full head | CertCall | Q logits [M][N] | chunk upper and lower bounds [2][M][chunks] | lists];
+// CertZero sits in the counter region at the start of the GEMM region.
 struct CertLayout {
   size_t gemm, state, logits, ub, list, total;
 };
@@ -161,7 +161,7 @@ CertLayout cert_layout(int64_t n, int64_t k, int64_t M) {
   c.state = c.gemm;
   c.logits = c.state + round256(sizeof(CertCall));
   c.ub = c.logits + round256((size_t)M * (size_t)n * sizeof(float));
-  c.list = c.ub + round256((size_t)M * (size_t)cert_chunks(n) * sizeof(float));
+  c.list = c.ub + round256(2 * (size_t)M * (size_t)cert_chunks(n) * sizeof(float));
   c.total = c.list + round256((size_t)M * W12_CERT_MAX_SURVIVORS * sizeof(uint32_t));
   return c;
 }
@@ -604,7 +604,8 @@ int w12_lmhead_argmax_certified(const w12_matrix* m, const float* bounds, const 
   int r = run_gemm(m, x, M, ldx, lq, m->n, W12_F32, W12_OP_GEMM_Q8, true, ws, c.gemm, nullptr, nullptr, stream);
   if (r != W12_OK) return r;
   // 2. bounds, survivors, exact rescoring, indices
-  const hipError_t e = launch_cert(m, x, ldx, (int)M, lq, bounds, z, cc, reinterpret_cast<float*>(wsb + c.ub),
+  float* ub = reinterpret_cast<float*>(wsb + c.ub);
+  const hipError_t e = launch_cert(m, x, ldx, (int)M, lq, bounds, z, cc, ub, ub + M * cert_chunks(m->n),
                                    reinterpret_cast<uint32_t*>(wsb + c.list), idx, max_logit, survivors,
                                    reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "certified head kernels");

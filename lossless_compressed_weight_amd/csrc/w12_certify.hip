@@ -19,10 +19,10 @@
 //
 // Kernels, in stream order after the Q pass:
 //   k_cert_lower   per (chunk of rows, activation row): ||x||, the chunk's
-//                  largest lower bound (atomic max per activation row) and its
-//                  largest upper bound (kept per chunk)
-//   k_cert_select  chunks whose largest upper bound reaches the best lower
-//                  bound list their surviving rows
+//                  largest lower and upper bounds (kept per chunk)
+//   k_cert_select  the best lower bound of the activation row (a maximum over
+//                  its chunks); chunks whose largest upper bound reaches it
+//                  list their surviving rows
 //   k_cert_rescore one wave per (activation row, survivor): exact dot product
 //                  from the record bytes and the escape list, 64-bit argmax
 //                  key; the row's last pair writes its index and maximum. A row
@@ -36,6 +36,7 @@ namespace {
 
 constexpr int kCertChunk = 2048;   // rows per chunk (8 per thread of 256)
 constexpr int kCertThreads = 256;
+static_assert(kCertChunk % kCertThreads == 0, "whole rows per thread");
 
 // Wave sums in a fixed order (butterfly over the 64 lanes).
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -146,17 +147,30 @@ struct CertArgs {
   const float* bounds;   // [N][2]: r_n, a_n
   CertZero* z;
   CertCall* cc;
-  float* ub_chunk;       // [M][chunks]
+  float* ub_chunk;       // [M][chunks]: each chunk's largest upper bound
+  float* lb_chunk;       // [M][chunks]: each chunk's largest lower bound
   uint32_t* list;        // [M][cap]
   int n, k, m, chunks, cap;
   double slack;
 };
 
+// Thread t sums x[t]^2, x[t + 256]^2, ... in order; the loads of eight
+// terms go out together (past K they are zero, which leaves the sum as it is).
 __device__ double row_norm(const uint16_t* x, int k, double* red) {
+  constexpr int kBatch = 8;
   double s = 0.0;
-  for (int i = threadIdx.x; i < k; i += kCertThreads) {
-    const double v = (double)bf16_to_f32(x[i]);
-    s += v * v;
+  for (int i0 = threadIdx.x; i0 < k; i0 += kBatch * kCertThreads) {
+    float v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + j * kCertThreads;
+      v[j] = i < k ? bf16_to_f32(x[i]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const double d = (double)v[j];
+      s += d * d;
+    }
   }
   s = wave_sum_f64(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
@@ -168,7 +182,9 @@ __device__ double row_norm(const uint16_t* x, int k, double* red) {
 }
 
 // Per (chunk of rows, activation row m): ||x_m||, the chunk's largest lower
-// bound (atomic max per activation row) and its largest upper bound.
+// and upper bounds. (One atomic maximum per activation row instead, from
+// every chunk, queued the chunks' workgroups on one cache line: 24 us at
+// M = 16 for the 151936-row head.)
 __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
   __shared__ double red[kCertThreads / 64];
   __shared__ float lo_w[kCertThreads / 64], hi_w[kCertThreads / 64];
@@ -180,11 +196,21 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
   }
   float lo = -__builtin_inff(), hi = -__builtin_inff();
   const int r0 = chunk * kCertChunk;
-  for (int i = threadIdx.x; i < kCertChunk; i += kCertThreads) {
-    const int row = r0 + i;
-    if (row >= a.n) break;
-    const double lq = (double)a.lq[(int64_t)m * a.n + row];
-    const double width = xn * ((double)a.bounds[2 * row] + a.slack * (double)a.bounds[2 * row + 1]);
+  // the thread's rows of the chunk: all their loads first, then the bounds
+  constexpr int kRows = kCertChunk / kCertThreads;
+  float lqv[kRows];
+  float2 bd[kRows];
+#pragma unroll
+  for (int j = 0; j < kRows; ++j) {
+    const int row = r0 + j * kCertThreads + (int)threadIdx.x;
+    lqv[j] = row < a.n ? a.lq[(int64_t)m * a.n + row] : 0.f;
+    bd[j] = row < a.n ? make_float2(a.bounds[2 * row], a.bounds[2 * row + 1]) : make_float2(0.f, 0.f);
+  }
+#pragma unroll
+  for (int j = 0; j < kRows; ++j) {
+    if (r0 + j * kCertThreads + (int)threadIdx.x >= a.n) break;
+    const double lq = (double)lqv[j];
+    const double width = xn * ((double)bd[j].x + a.slack * (double)bd[j].y);
     const double lower = isfinite(width) ? lq - width : -__builtin_inf();
     const double upper = lq + width;
     lo = fmaxf(lo, __double2float_rd(lower));                 // NaN ignored
@@ -206,7 +232,7 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
       lo = fmaxf(lo, lo_w[w]);
       hi = fmaxf(hi, hi_w[w]);
     }
-    __hip_atomic_fetch_max(&a.z->lower[m], ord32(lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.lb_chunk[(int64_t)m * a.chunks + chunk] = lo;
     a.ub_chunk[(int64_t)m * a.chunks + chunk] = hi;
   }
 }
@@ -214,8 +240,25 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
 // Chunks whose largest upper bound reaches the best lower bound list their
 // surviving rows (the count may pass the cap; entries past it are dropped).
 __global__ __launch_bounds__(kCertThreads) void k_cert_select(CertArgs a) {
+  __shared__ uint32_t lo_w[kCertThreads / 64];
   const int chunk = blockIdx.x, m = blockIdx.y;
-  const float best_lower = unord32(a.z->lower[m]);
+  // the activation row's best lower bound: the largest of its chunks' (as
+  // order-preserving keys, so the maximum does not depend on the order)
+  uint32_t key = 0u;
+  for (int c = threadIdx.x; c < a.chunks; c += kCertThreads) {
+    const uint32_t kc = ord32(a.lb_chunk[(int64_t)m * a.chunks + c]);
+    key = kc > key ? kc : key;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t t = __shfl_xor(key, o, 64);
+    key = t > key ? t : key;
+  }
+  if ((threadIdx.x & 63) == 0) lo_w[threadIdx.x >> 6] = key;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kCertThreads / 64; ++w) key = lo_w[w] > key ? lo_w[w] : key;
+  const float best_lower = unord32(key);
   if (a.ub_chunk[(int64_t)m * a.chunks + chunk] < best_lower) return;  // nothing here can win
   const double xn = a.cc->xnorm[m];
   const int lane = threadIdx.x & 63;
@@ -275,7 +318,6 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_rescore(RescoreArgs a) {
   if (blockIdx.x == 0 && threadIdx.x < 64) {
     if (threadIdx.x == 0)
       __hip_atomic_store(&a.cc->flag, fallback ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane < kCertMaxM) a.z->lower[lane] = 0u;  // read by no kernel after k_cert_select
     if (lane < a.m && (fallback || c == 0u)) {
       // the full head answers (or, with no survivor at all, which the bounds
       // rule out, index 0): only the counts are reported here
@@ -380,7 +422,8 @@ hipError_t launch_cert_bounds(const w12_matrix* m, float* bounds, hipStream_t s)
 int cert_chunks(int64_t n) { return (int)((n + kCertChunk - 1) / kCertChunk); }
 
 hipError_t launch_cert(const w12_matrix* mat, const uint16_t* x, int64_t ldx, int M, const float* lq,
-                       const float* bounds, CertZero* z, CertCall* cc, float* ub_chunk, uint32_t* list, int32_t* idx,
+                       const float* bounds, CertZero* z, CertCall* cc, float* ub_chunk, float* lb_chunk,
+                       uint32_t* list, int32_t* idx,
                        float* maxv, int32_t* survivors, hipStream_t s) {
   CertArgs a{};
   a.x = x;
@@ -390,6 +433,7 @@ hipError_t launch_cert(const w12_matrix* mat, const uint16_t* x, int64_t ldx, in
   a.z = z;
   a.cc = cc;
   a.ub_chunk = ub_chunk;
+  a.lb_chunk = lb_chunk;
   a.list = list;
   a.n = (int)mat->n;
   a.k = (int)mat->k;

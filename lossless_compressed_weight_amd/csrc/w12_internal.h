@@ -254,13 +254,12 @@ hipError_t launch_rows_argmax(const float* y, int64_t ldy, int n, int M, unsigne
 // ------------------------------------------------------------------ certified LM head
 // State of the certified head (w12_certify.hip). CertZero accumulates, so it
 // lives in the counter region (kCertZeroOffset): zero before a workspace's
-// first use and left zero by every call (k_cert_rescore clears the lower
-// bounds, a row's last rescored pair its key and done count). CertCall is
-// written by every call before it is read.
+// first use and left zero by every call (a row's last rescored pair clears
+// its key and done count). CertCall is written by every call before it is
+// read.
 constexpr int kCertMaxM = 64;
 struct CertZero {
   unsigned long long best[kCertMaxM];  // argmax keys of the rescored rows
-  uint32_t lower[kCertMaxM];           // order-preserving key of the best lower bound
   uint32_t done[kCertMaxM];            // survivors rescored
 };
 struct CertCall {
@@ -272,8 +271,8 @@ static_assert(kCertZeroOffset + sizeof(CertZero) <= kCounterBytes, "counter regi
 int cert_chunks(int64_t n);
 hipError_t launch_cert_bounds(const w12_matrix* m, float* bounds, hipStream_t s);
 hipError_t launch_cert(const w12_matrix* mat, const uint16_t* x, int64_t ldx, int M, const float* lq,
-                       const float* bounds, CertZero* z, CertCall* cc, float* ub_chunk, uint32_t* list, int32_t* idx,
-                       float* maxv, int32_t* survivors, hipStream_t s);
+                       const float* bounds, CertZero* z, CertCall* cc, float* ub_chunk, float* lb_chunk,
+                       uint32_t* list, int32_t* idx, float* maxv, int32_t* survivors, hipStream_t s);
 
 // ------------------------------------------------------------------ stream kernel
 // The MFMA stream kernel (w12_gemm_mx.hip): eight streaming waves per
