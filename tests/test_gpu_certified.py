@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import dev16, log, o, w12
+from gpu_util import check_f32, dev16, log, o, w12
 
 pytestmark = pytest.mark.gpu
 
@@ -141,24 +141,28 @@ def test_certified_head_infinite_rows():
     assert int(sv.min()) >= 3                       # the three infinite rows always survive
 
 
-def test_certified_head_falls_back_when_too_many_survive():
+@pytest.mark.parametrize("m", [4, 20])
+def test_certified_head_falls_back_when_too_many_survive(m):
     """Identical rows: every logit ties, every row survives (1024 > cap), so
-    the full head runs and the lowest index wins; then a normal call on the
+    the full head runs (the fused argmax up to 16 activation rows, the
+    two-pass one beyond) and the lowest index wins; then a normal call on the
     same workspace is certified again (the state was cleared)."""
     base = synth.workload_matrix(0, 0)
     w = np.tile(base[7:8], (1024, 1))
-    x = synth.make_activations(4, 1024, seed=5)
+    x = synth.make_activations(m, 1024, seed=5)
     y, yq, r, a = _oracle(w, x)
     mat = w12.encode(dev16(w))
     bounds = _check_bounds(mat, r, a)
-    ws = w12.new_workspace(w12.OP_LMHEAD_CERTIFIED, 1024, 1024, 4)
-    idx = torch.empty(4, dtype=torch.int32, device="cuda")
-    mx = torch.empty(4, dtype=torch.float32, device="cuda")
-    sv = torch.empty(4, dtype=torch.int32, device="cuda")
+    ws = w12.new_workspace(w12.OP_LMHEAD_CERTIFIED, 1024, 1024, m)
+    idx = torch.empty(m, dtype=torch.int32, device="cuda")
+    mx = torch.empty(m, dtype=torch.float32, device="cuda")
+    sv = torch.empty(m, dtype=torch.int32, device="cuda")
     for rep in range(2):
         w12.w12_lmhead_argmax_certified(mat, bounds, dev16(x), idx, mx, sv, ws)
-        assert idx.cpu().numpy().tolist() == [0, 0, 0, 0]
-        assert sv.cpu().numpy().tolist() == [1024] * 4
+        assert idx.cpu().numpy().tolist() == [0] * m
+        assert sv.cpu().numpy().tolist() == [1024] * m
+        # the maximum is the tied logit itself, within the oracle's tolerance
+        check_f32(mx.cpu().numpy()[:, None], y[:, :1], f"fallback M={m} max")
     mat2 = w12.encode(dev16(base))
     y2, yq2, r2, a2 = _oracle(base, x)
     b2 = w12.certify_bounds(mat2)
