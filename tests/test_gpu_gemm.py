@@ -207,18 +207,26 @@ def test_deterministic_repeats():
         assert torch.equal(qa, qb)
 
 
-def test_strided_activations_and_outputs():
+@pytest.mark.parametrize("path", [0, 2, 3])
+def test_strided_activations_and_outputs(path):
+    """x and y with row strides past K and N, on the library's choice and on
+    each MFMA kernel forced (both read row-major x themselves up to 16 rows,
+    the stream kernel at every M)."""
     w = synth.workload_matrix(0, 0)
     mat = w12.encode(dev16(w))
-    for m in (3, 20):
-        xfull = synth.make_activations(m, 1024 + 64, seed=m)
-        xd = dev16(xfull)[:, :1024]                                       # ldx = 1088
-        y = torch.full((m, 1024 + 32), -7.0, dtype=torch.float32, device="cuda")
-        ws = w12.new_workspace(w12.OP_GEMM, 1024, 1024, m)
-        w12.w12_gemm(mat, xd, y[:, :1024], ws)
-        yh = y.cpu().numpy()
-        check_f32(yh[:, :1024], o.gemm_ref(xfull[:, :1024], w), f"strided M={m}")
-        assert np.all(yh[:, 1024:] == -7.0)                               # nothing written past N
+    old = w12.set_tuning(w12.TUNE_PATH, path)
+    try:
+        for m in (3, 16, 20, 32):
+            xfull = synth.make_activations(m, 1024 + 64, seed=m)
+            xd = dev16(xfull)[:, :1024]                                   # ldx = 1088
+            y = torch.full((m, 1024 + 32), -7.0, dtype=torch.float32, device="cuda")
+            ws = w12.new_workspace(w12.OP_GEMM, 1024, 1024, m)
+            w12.w12_gemm(mat, xd, y[:, :1024], ws)
+            yh = y.cpu().numpy()
+            check_f32(yh[:, :1024], o.gemm_ref(xfull[:, :1024], w), f"strided M={m} path {path}")
+            assert np.all(yh[:, 1024:] == -7.0)                           # nothing written past N
+    finally:
+        w12.set_tuning(w12.TUNE_PATH, old)
 
 
 @pytest.mark.parametrize("m", [1, 8, 16, 32])
