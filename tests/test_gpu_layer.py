@@ -70,7 +70,7 @@ def _check_group(g, x, y_f32, y_bf16):
         col += n
 
 
-@pytest.mark.parametrize("m", [32, 64])
+@pytest.mark.parametrize("m", [4, 16, 32, 64])
 def test_fused_layer_matches_oracle(m):
     xs = _inputs(m)
     for g, mat in _fused().items():
