@@ -240,7 +240,7 @@ int run_mx(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void*
 
 int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
              int op, bool fix, void* ws, size_t ws_bytes, int32_t* idx, float* maxv, void* stream,
-             const uint32_t* gate = nullptr, int force_kernel = 0);
+             const uint32_t* gate = nullptr, int force_kernel = 0, uint16_t* dense_xt = nullptr);
 
 // Dense escapes: activations transposed for the fix-up, the GEMM without escape
 // work into fp32 sums, then the fix-up kernel writes y.
@@ -253,9 +253,8 @@ int run_dense(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, vo
   uint16_t* xt = reinterpret_cast<uint16_t*>(wsb + d.xt);
   const int mm = (int)(((M + 15) / 16) * 16);
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_xpose(x, ldx, (int)M, mm, (int)m->k, xt, nullptr, nullptr, st);
-  if (e != hipSuccess) return hip_fail(e, "dense escapes: activation transpose launch");
-  const int r = run_gemm(m, x, M, ldx, a, m->n, W12_F32, op, false, ws, d.main, nullptr, nullptr, stream);
+  // the GEMM call also writes xT, in the same launch as its own copies of x
+  const int r = run_gemm(m, x, M, ldx, a, m->n, W12_F32, op, false, ws, d.main, nullptr, nullptr, stream, nullptr, 0, xt);
   if (r != W12_OK) return r;
   FixParams p{};
   p.a = a;
@@ -270,7 +269,7 @@ int run_dense(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, vo
   p.y_f32 = y_dtype == W12_F32;
   p.q = op == W12_OP_GEMM_Q8;
   p.slices = fix_slices(m->n, m->n_esc, (int)M);
-  e = launch_fix_dense(p, st);
+  const hipError_t e = launch_fix_dense(p, st);
   if (e != hipSuccess) return hip_fail(e, "dense escapes: fix-up launch");
   return W12_OK;
 }
@@ -302,7 +301,10 @@ int run_argmax_two_pass(const w12_matrix* m, const uint16_t* x, int64_t M, int64
 // force_kernel: 0, or the kernel to run whatever the usual choice.
 int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, void* y, int64_t ldy, int y_dtype,
              int op, bool fix, void* ws, size_t ws_bytes, int32_t* idx, float* maxv, void* stream,
-             const uint32_t* gate, int force_kernel) {
+             const uint32_t* gate, int force_kernel, uint16_t* dense_xt) {
+  // dense_xt: the dense path's transposed copy of x ([K][mm], rows past M
+  // zero), written by this call's activation pre-pass (a launch of its own
+  // before the stream kernel, which has none)
   if (op == W12_OP_LMHEAD_ARGMAX && M > kFusedArgmaxMaxM)
     return run_argmax_two_pass(m, x, M, ldx, fix, ws, ws_bytes, idx, maxv, stream, gate);
   if (!gate && !force_kernel && dense_path(m, op, fix))
@@ -311,7 +313,14 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   const int kernel = force_kernel ? force_kernel
                      : gate     ? (pl.mfma ? W12_KERNEL_MFMA_HELPER : W12_KERNEL_GEMV)
                                 : choose_kernel(m->n, m->k, m->n_esc, M, op, fix, pl);
-  if (kernel == W12_KERNEL_MFMA_STREAM) return run_mx(m, x, M, ldx, y, ldy, y_dtype, op, fix, ws, ws_bytes, stream);
+  if (kernel == W12_KERNEL_MFMA_STREAM) {
+    if (dense_xt) {
+      const hipError_t ex = launch_xpose(x, ldx, (int)M, (int)(((M + 15) / 16) * 16), (int)m->k, dense_xt, nullptr,
+                                         nullptr, reinterpret_cast<hipStream_t>(stream));
+      if (ex != hipSuccess) return hip_fail(ex, "dense escapes: activation transpose launch");
+    }
+    return run_mx(m, x, M, ldx, y, ldy, y_dtype, op, fix, ws, ws_bytes, stream);
+  }
   if (!pl.mfma && M > 16) return W12_E_M_RANGE;
   const size_t need = gemm_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need)) return W12_E_WORKSPACE;
@@ -345,12 +354,13 @@ int run_gemm(const w12_matrix* m, const uint16_t* x, int64_t M, int64_t ldx, voi
   p.xt = nullptr;
   p.xk = nullptr;
   const XCopies xc = x_copies(m, pl, M, p.fix != 0);
-  if (xc.xt || xc.xk) {
+  if (xc.xt || xc.xk || dense_xt) {
     const int64_t mm = ((M + 15) / 16) * 16;
     char* xt_at = wsb + round256(pl.ctr_bytes) + round256(pl.part_bytes) + round256(pl.key_bytes);
     uint16_t* xt = xc.xt ? reinterpret_cast<uint16_t*>(xt_at) : nullptr;
     uint16_t* xk = xc.xk ? reinterpret_cast<uint16_t*>(xt_at + round256(pl.xt_bytes)) : nullptr;
-    const hipError_t ex = launch_xpose(x, ldx, (int)M, (int)mm, (int)m->k, xt, xk, gate, st);
+    // the dense path's xT takes the place of the kernel's own, which it does not read (no escape work)
+    const hipError_t ex = launch_xpose(x, ldx, (int)M, (int)mm, (int)m->k, dense_xt ? dense_xt : xt, xk, gate, st);
     if (ex != hipSuccess) return hip_fail(ex, "activation transpose launch");
     p.xt = xt;
     p.xk = xk;
