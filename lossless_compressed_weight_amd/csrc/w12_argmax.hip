@@ -25,14 +25,16 @@ __global__ __launch_bounds__(kArgThreads) void k_rows_argmax(const float* __rest
   const int m = blockIdx.y, c0 = blockIdx.x * kArgChunk;
   const float* yr = y + (int64_t)m * ldy;
   unsigned long long best = 0ull;
-  // four 16-byte loads per thread, all in flight together (N is a multiple of
-  // 16, so a piece is wholly inside or wholly past the row)
+  // sixteen 16-byte loads per thread, all in flight together: N is a multiple
+  // of 16, so a piece is wholly inside or wholly past the row, and a piece
+  // past the row loads the row's last piece instead (no branch, so no wait
+  // between the loads) and is skipped below
   constexpr int kPieces = kArgChunk / (4 * kArgThreads);
   float4 v[kPieces];
 #pragma unroll
   for (int j = 0; j < kPieces; ++j) {
     const int c = c0 + 4 * (j * kArgThreads + (int)threadIdx.x);
-    v[j] = c < n ? *reinterpret_cast<const float4*>(yr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[j] = *reinterpret_cast<const float4*>(yr + min(c, n - 4));
   }
 #pragma unroll
   for (int j = 0; j < kPieces; ++j) {

@@ -154,17 +154,19 @@ struct CertArgs {
   double slack;
 };
 
-// Thread t sums x[t]^2, x[t + 256]^2, ... in order; the loads of eight
-// terms go out together (past K they are zero, which leaves the sum as it is).
+// Thread t sums x[t]^2, x[t + 256]^2, ... in order; the loads of 24 terms go
+// out together, all of a row up to K = 6144 (past K they are zero, which
+// leaves the sum as it is).
 __device__ double row_norm(const uint16_t* x, int k, double* red) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 24;
   double s = 0.0;
   for (int i0 = threadIdx.x; i0 < k; i0 += kBatch * kCertThreads) {
     float v[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int i = i0 + j * kCertThreads;
-      v[j] = i < k ? bf16_to_f32(x[i]) : 0.f;
+      const float xi = bf16_to_f32(x[min(i, k - 1)]);  // clamped in bounds, so the loads carry no branches
+      v[j] = i < k ? xi : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -189,23 +191,25 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_lower(CertArgs a) {
   __shared__ double red[kCertThreads / 64];
   __shared__ float lo_w[kCertThreads / 64], hi_w[kCertThreads / 64];
   const int chunk = blockIdx.x, m = blockIdx.y;
+  const int r0 = chunk * kCertChunk;
+  // the thread's rows of the chunk: their loads go out first, with those of
+  // x's norm, then the bounds
+  constexpr int kRows = kCertChunk / kCertThreads;
+  float lqv[kRows];
+  float2 bd[kRows];
+#pragma unroll
+  for (int j = 0; j < kRows; ++j) {
+    // rows past N load row N - 1 (in bounds, no branch) and are skipped below
+    const int row = min(r0 + j * kCertThreads + (int)threadIdx.x, a.n - 1);
+    lqv[j] = a.lq[(int64_t)m * a.n + row];
+    bd[j] = make_float2(a.bounds[2 * row], a.bounds[2 * row + 1]);
+  }
   const double xn = row_norm(a.x + (int64_t)m * a.ldx, a.k, red);
   if (chunk == 0 && threadIdx.x == 0) {
     a.cc->xnorm[m] = xn;
     a.cc->count[m] = 0u;  // the survivors are counted by k_cert_select
   }
   float lo = -__builtin_inff(), hi = -__builtin_inff();
-  const int r0 = chunk * kCertChunk;
-  // the thread's rows of the chunk: all their loads first, then the bounds
-  constexpr int kRows = kCertChunk / kCertThreads;
-  float lqv[kRows];
-  float2 bd[kRows];
-#pragma unroll
-  for (int j = 0; j < kRows; ++j) {
-    const int row = r0 + j * kCertThreads + (int)threadIdx.x;
-    lqv[j] = row < a.n ? a.lq[(int64_t)m * a.n + row] : 0.f;
-    bd[j] = row < a.n ? make_float2(a.bounds[2 * row], a.bounds[2 * row + 1]) : make_float2(0.f, 0.f);
-  }
 #pragma unroll
   for (int j = 0; j < kRows; ++j) {
     if (r0 + j * kCertThreads + (int)threadIdx.x >= a.n) break;
@@ -263,14 +267,22 @@ __global__ __launch_bounds__(kCertThreads) void k_cert_select(CertArgs a) {
   const double xn = a.cc->xnorm[m];
   const int lane = threadIdx.x & 63;
   const int r0 = chunk * kCertChunk;
-  for (int base = 0; base < kCertChunk; base += kCertThreads) {
-    const int row = r0 + base + threadIdx.x;
-    bool keep = false;
-    if (row < a.n) {
-      const double lq = (double)a.lq[(int64_t)m * a.n + row];
-      const double width = xn * ((double)a.bounds[2 * row] + a.slack * (double)a.bounds[2 * row + 1]);
-      keep = !(lq + width < (double)best_lower);
-    }
+  // the thread's rows: all loads first (rows past N load row N - 1, in bounds,
+  // and are not kept), then the survivors are listed
+  constexpr int kRows = kCertChunk / kCertThreads;
+  float lqv[kRows];
+  float2 bd[kRows];
+#pragma unroll
+  for (int j = 0; j < kRows; ++j) {
+    const int row = min(r0 + j * kCertThreads + (int)threadIdx.x, a.n - 1);
+    lqv[j] = a.lq[(int64_t)m * a.n + row];
+    bd[j] = make_float2(a.bounds[2 * row], a.bounds[2 * row + 1]);
+  }
+#pragma unroll
+  for (int j = 0; j < kRows; ++j) {
+    const int row = r0 + j * kCertThreads + (int)threadIdx.x;
+    const double width = xn * ((double)bd[j].x + a.slack * (double)bd[j].y);
+    const bool keep = row < a.n && !((double)lqv[j] + width < (double)best_lower);
     const uint64_t ballot = __ballot(keep);
     if (ballot == 0) continue;
     uint32_t pos0 = 0;

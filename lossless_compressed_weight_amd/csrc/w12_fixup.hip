@@ -146,7 +146,12 @@ __global__ __launch_bounds__(kFixThreads) void k_fix_dense(FixParams p) {
       XPiece<V> xv[kFixBatch];
 #pragma unroll
       for (int j = 0; j < kFixBatch; ++j) {
-        if ((uint32_t)j < left) {
+        if constexpr (V == 1) {
+          // one activation row: the compiler would wait on each conditional
+          // 2-byte load before the next, so every lane loads (an entry past
+          // its slice reads column 0, in bounds) and the FMAs skip it below
+          xv[j] = load_piece<V>(reinterpret_cast<const uint16_t*>(xtb + ((uint32_t)j < left ? ent[j].x : 0u) * xrow));
+        } else if ((uint32_t)j < left) {
           xv[j] = load_piece<V>(reinterpret_cast<const uint16_t*>(xtb + ent[j].x * xrow));
         } else {
 #pragma unroll
