@@ -1283,7 +1283,7 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t rw = 8u * h + (uint32_t)(lane >> 3), rr = (uint32_t)(lane & 15);
-      xo[h] = 2u * ((uint32_t)min((int)rw, a.m - 1) * (uint32_t)a.ldx + (uint32_t)(wave * 64 + (lane & 7) * 8));
+      xo[h] = 2u * ((uint32_t)min((int)rw, a.m - 1) * (uint32_t)a.ldx + (uint32_t)((lane & 7) * 8));
       xs_w[h] = rw * 128u + ((((uint32_t)lane & 7u) ^ ((rw >> 1) & 7u)) << 4);
       xs_r[h] = rr * 128u + ((((uint32_t)(lane >> 4) * 2u + h) ^ ((rr >> 1) & 7u)) << 4);
     }
@@ -1291,11 +1291,22 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
   const char* xrow = reinterpret_cast<const char*>(a.x);
   const uint8_t* blk = a.rec + (int64_t)s * a.kb * kRecBytes;
   const uint32_t blk_stride = (uint32_t)(a.kb * kRecBytes);
-  auto load = [&](MfmaStage<MT, RG, Q>& st, int kk) {
-    const int c = kk * 4 + wave;
+  // The wave's chunks: chunk w of every unit, except that wave 0 (which
+  // shares its SIMD with the helper wave and streams ~6-8% slower) leaves
+  // its chunk of the segment's last d units to waves 1, 2, 3 in turn. Each
+  // wave's sums cover whatever columns it takes, and the helper adds the four
+  // in a fixed order, so the result stays deterministic.
+  const int nu = k1 - k0;
+  const int d = (nu + 8) >> 4;
+  const int items = wave == 0 ? nu - d : nu + (d > wave - 1 ? (d - wave + 3) / 3 : 0);
+  auto chunk_of = [&](int i) {
+    return wave == 0 ? 4 * (k0 + i) : (i < nu ? 4 * (k0 + i) + wave : 4 * (k1 - d + (wave - 1) + 3 * (i - nu)));
+  };
+  auto load = [&](MfmaStage<MT, RG, Q>& st, int i) {
+    const int c = chunk_of(i);
     if constexpr (MT == 1) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) st.x[0][h] = *reinterpret_cast<const uint4*>(xrow + (xo[h] + (uint32_t)kk * 512u));
+      for (int h = 0; h < 2; ++h) st.x[0][h] = *reinterpret_cast<const uint4*>(xrow + (xo[h] + (uint32_t)c * 128u));
     } else {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -1343,7 +1354,7 @@ __device__ __forceinline__ void mfma_group(const GemmParams& a, int s, int k0, i
       }
     }
   };
-  pipeline<MfmaStage<MT, RG, Q>>(k0, k1, load, compute);
+  pipeline<MfmaStage<MT, RG, Q>>(0, items, load, compute);
   if (seg >= 2) lds_wait_geq(consumed, (uint32_t)(seg - 1));
   // C layout of a 16x16 MFMA: lane l holds rows 4 (l/16) + i, column l % 16.
 #pragma unroll

@@ -313,20 +313,23 @@ def test_lmhead_argmax_whole_tiles(m):
     assert np.all(idx[lead] == 3000)
 
 
-def test_lmhead_argmax_planted_ties_and_negatives():
-    """All-negative logits, exact ties (lowest index wins) and -0 vs +0."""
+@pytest.mark.parametrize("m", [2, 20])
+def test_lmhead_argmax_planted_ties_and_negatives(m):
+    """All-negative logits, exact ties (lowest index wins) and -0 vs +0; at
+    M = 20 through the stored-logits pass, whose workgroup reads pieces past
+    the 64 columns of a row (they re-read the row's last piece, unused)."""
     k = 512
     w = np.zeros((64, k), np.uint16)
     w[:, 0] = 0xBF80                                                     # every logit = -x0
     w[10, 0] = 0xBF00                                                    # -0.5: the max for x0 > 0
     w[40, 0] = 0xBF00                                                    # tie with row 10
     mat = w12.encode(dev16(w))
-    x = np.zeros((2, k), np.uint16)
-    x[0, 0] = 0x4000                                                     # 2.0
-    x[1, 0] = 0x0000                                                     # all logits +-0 -> row 0
+    x = np.zeros((m, k), np.uint16)
+    x[0::2, 0] = 0x4000                                                  # 2.0
+    x[1::2, 0] = 0x0000                                                  # all logits +-0 -> row 0
     idx, mx = w12.lmhead_argmax(mat, dev16(x))
-    assert idx.cpu().tolist() == [10, 0]
-    assert mx.cpu().tolist() == [-1.0, 0.0]
+    assert idx.cpu().tolist() == [10, 0] * (m // 2)
+    assert mx.cpu().tolist() == [-1.0, 0.0] * (m // 2)
 
 
 def test_oracle_encoded_records_drive_the_gemm():
