@@ -121,3 +121,28 @@ def test_dense_path_workspace_reuse_and_strides():
             assert np.all(yh[:, n:] == -7.0)
     torch.cuda.synchronize()
     assert int(ws[: w12.WS_COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("m", [1, 32])
+def test_dense_path_escape_lists_beyond_one_lds_piece(m):
+    """Many escapes per row on a tall matrix: the slices per row are capped so
+    that the fix-up's lanes stay within one pass of the device, so each
+    workgroup takes 32 or more rows and more than the 2048 escape entries that
+    one LDS piece holds; the lists are walked across several pieces, with
+    slices that straddle a piece boundary."""
+    n, k = 20480, 2048
+    w = synth.workload_matrix(3, 0, rows=slice(0, n))[:, :k].copy()
+    rng = np.random.default_rng(11)
+    hit = rng.random(w.shape) < 0.06
+    e = (w >> 7) & 0xFF
+    # outliers 2^12 above their neighbours (exponent field + 12, exact): escapes
+    w = np.where(hit & (e > 0) & (e < 240), w + (12 << 7), w).astype(np.uint16)
+    mat = w12.encode(dev16(w))
+    assert mat.n_esc > 100 * n                       # > 3200 entries in any 32 rows
+    assert w12.plan_info(mat, w12.OP_GEMM, m)["fixup"] == 1
+    x = synth.make_activations(m, k, seed=7300 + m)
+    log(f"[dense] {n}x{k} n_esc={mat.n_esc} M={m}")
+    yf, yb = gemm_both(mat, dev16(x))
+    y64 = o.gemm_ref(x, w)
+    check_f32(yf, y64, f"dense pieces M={m}")
+    check_bf16(yb, yf, y64, f"dense pieces M={m}")
