@@ -74,12 +74,17 @@ def test_dense_onehot_rows_reproduce_columns_exactly():
     enc = o.encode(w)
     mat = w12.encode(dev16(w))
     cols = np.unique(np.concatenate([[0, 1, 511, 512, 1023], np.unique(enc.esc["col"])[:59]]))
+    qv = o.q_view_escapes_bits(enc)
     for start in range(0, len(cols), 32):
         cc = cols[start:start + 32]
         x = np.zeros((len(cc), w.shape[1]), np.uint16)
         x[np.arange(len(cc)), cc] = 0x3F80
         y = w12.gemm(mat, dev16(x), torch.float32).cpu().numpy()
         assert np.array_equal(y.astype(np.float64), o.bf16_to_f64(w[:, cc]).T), f"cols {cc}"
+        # the Q pass with escapes through the same fix-up: the Q view with the
+        # escapes' exact values, column for column
+        yq = w12.gemm_q8(mat, dev16(x), torch.float32, apply_escapes=True).cpu().numpy()
+        assert np.array_equal(yq.astype(np.float64), o.bf16_to_f64(qv[:, cc]).T), f"Q cols {cc}"
 
 
 def test_dense_non_finite_weights():

@@ -207,6 +207,25 @@ def test_deterministic_repeats():
         assert torch.equal(qa, qb)
 
 
+def test_deterministic_repeats_whole_tiles():
+    """17408 x 5120 (272 whole tiles): the helper-wave kernel at every M from
+    3 (its streaming waves' fixed share of columns, the split tiles' exchange)
+    and the GEMV below; repeated calls, over two copies of the matrix, give
+    the same bits."""
+    w = synth.workload_matrix(1, 0)
+    mat = w12.encode(dev16(w))
+    mat2 = w12.W12Matrix(mat.n, mat.k, mat.records.clone(), mat.e_top.clone(), mat.row_ptr.clone(),
+                         mat.esc.clone(), mat.n_esc)
+    for m in (1, 3, 16, 17, 32, 64):
+        log(f"[repeats] 17408x5120 M={m} {w12.plan_info(mat, w12.OP_GEMM, m)['kernel_name']}")
+        x = dev16(synth.make_activations(m, w.shape[1], seed=40 + m))
+        a = w12.gemm(mat, x, torch.float32)
+        for rep in range(2):
+            assert torch.equal(w12.gemm(mat2 if rep else mat, x, torch.float32), a)
+            assert torch.equal(w12.gemm_q8(mat, x, torch.float32, apply_escapes=True),
+                               w12.gemm_q8(mat2, x, torch.float32, apply_escapes=True))
+
+
 @pytest.mark.parametrize("path", [0, 2, 3])
 def test_strided_activations_and_outputs(path):
     """x and y with row strides past K and N, on the library's choice and on
