@@ -97,6 +97,8 @@ CASES = {
     "ragged_48": lambda: synth.workload_matrix(0, 0)[:48],
     "stress_rows": lambda: synth.workload_matrix(4, 0, rows=slice(0, 512)),
     "lm_head_rows": lambda: synth.workload_matrix(3, 0, rows=slice(0, 4096)),
+    # K = 17408: the norm of x takes several passes of the bound kernel's loads
+    "wide_k": lambda: synth.workload_matrix(1, 2, rows=slice(0, 512)),
 }
 
 
