@@ -104,8 +104,9 @@ bool dense_path(const w12_matrix* m, int op, bool fix) {
 // helper-wave kernel takes the rest (whole tiles per workgroup, whose escape
 // work and exchanges its helper wave overlaps with the stream), the fused
 // argmax, dense escapes and very long rows. Measured per call on MI355X at
-// M = 32: 6144 x 5120 21.0 vs 23.9 us, 5120 x 6144 20.6 vs 24.0,
-// 5120 x 17408 37.4 vs 37.5, 17408 x 5120 37.3 vs 32.2 (stream vs helper).
+// M = 32: 6144 x 5120 19.6 vs 24.2 us, 5120 x 6144 19.2 vs 23.6,
+// 5120 x 17408 35.6 vs 37.7, 17408 x 5120 35.8 vs 32.4 (stream vs helper);
+// the same order at M = 24, 48 and 64.
 // The copies of x that one activation transpose kernel writes before the
 // helper-wave MFMA kernel: beyond 16 activation rows its B operands in operand
 // order (xk; up to 16 rows the kernel stages x through LDS itself), and, with
